@@ -1,0 +1,289 @@
+"""Independent checks that pin the fp64 oracle to the mathematics.
+
+Each ``pin_*`` function takes the oracle module (or a stand-in with the same
+functions) and raises AssertionError when the oracle disagrees with something
+other than itself: closed forms, exhaustive integer properties, a 50-digit
+Decimal brute force, torch's float64 scaled_dot_product_attention, or a
+metamorphic relation. ``test_oracle.py`` runs them on the real oracle and
+``test_oracle_mutants.py`` runs them on oracles with planted mistakes, which
+every mutant must fail.
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# split bounds: exhaustive integer properties
+# --------------------------------------------------------------------------
+def pin_split_bounds(orc, max_len: int = 120):
+    """Proportional bounds (decode_attention_splitkv.py, split segment): for
+    every 1 <= ns <= L the splits tile [0, L) in order, each has floor(L/ns)
+    or ceil(L/ns) keys, exactly L mod ns of them have the larger size, and
+    split s starts at floor(L*s/ns). ns > L and ns < 1 raise."""
+    for L in range(1, max_len + 1):
+        for ns in range(1, L + 1):
+            b = orc.split_bounds(L, ns)
+            assert len(b) == ns
+            assert b[0][0] == 0 and b[-1][1] == L
+            sizes = [e - a for a, e in b]
+            for (a0, e0), (a1, _) in zip(b, b[1:]):
+                assert e0 == a1
+            lo, hi = L // ns, -(-L // ns)
+            assert all(s in (lo, hi) for s in sizes), (L, ns, sizes)
+            assert sum(1 for s in sizes if s == hi and hi != lo) == (L % ns)
+            assert min(sizes) >= 1
+            for s, (a, _) in enumerate(b):
+                assert a == math.floor(L * s / ns) if L * s < 2 ** 52 else True
+        for bad in (L + 1, L + 7):
+            try:
+                orc.split_bounds(L, bad)
+            except ValueError:
+                pass
+            else:
+                raise AssertionError(f"split_bounds({L},{bad}) must raise")
+    for bad in (0, -1):
+        try:
+            orc.split_bounds(10, bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("num_splits < 1 must raise")
+    # 64-bit-sized products stay exact (Python ints).
+    big = orc.split_bounds(2 ** 40 + 3, 7)
+    assert big[3][0] == (2 ** 40 + 3) * 3 // 7
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def pin_closed_forms(orc):
+    rng = _rng(1)
+    D = 16
+    # One key: softmax is 1, the output is that key's value exactly.
+    q = rng.standard_normal((3, D))
+    k = rng.standard_normal((1, D))
+    v = rng.standard_normal((1, D))
+    o = orc.attention_rows(q, k, v, 0.7)
+    assert np.array_equal(o, np.broadcast_to(v, (3, D))), "L=1 must return v0"
+    # Zero query: uniform weights, output = mean of V, lse_s = ln(count_s).
+    L = 37
+    k = rng.standard_normal((L, D))
+    v = rng.standard_normal((L, D))
+    q0 = np.zeros((2, D))
+    o = orc.attention_rows(q0, k, v, 0.3)
+    assert np.abs(o - v.mean(axis=0)).max() < 1e-14
+    op, lse = orc.split_partials_rows(q0, k, v, 5, 0.3)
+    for s, (a, e) in enumerate(orc.split_bounds(L, 5)):
+        assert np.abs(lse[s] - math.log(e - a)).max() < 1e-14
+        assert np.abs(op[:, s, :] - v[a:e].mean(axis=0)).max() < 1e-14
+    # Zero keys: same as zero query.
+    o = orc.attention_rows(rng.standard_normal((2, D)), np.zeros((L, D)), v, 0.3)
+    assert np.abs(o - v.mean(axis=0)).max() < 1e-14
+    # Two keys: o = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1.
+    q = rng.standard_normal((4, D))
+    k = rng.standard_normal((2, D))
+    v = rng.standard_normal((2, D))
+    sc = 0.25
+    o = orc.attention_rows(q, k, v, sc)
+    for r in range(4):
+        s0, s1 = sc * float(q[r] @ k[0]), sc * float(q[r] @ k[1])
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        assert np.abs(o[r] - (w0 * v[0] + w1 * v[1])).max() < 1e-14
+    # A dominant key (score larger by >= 60 than all others) gives its value.
+    k = rng.standard_normal((50, D)) * 0.01
+    q = np.zeros((1, D)); q[0, 0] = 1.0
+    k[17, 0] = 6000.0
+    v = rng.standard_normal((50, D))
+    o = orc.attention_rows(q, k, v, 0.01)
+    # every other key has weight < exp(-59), so only rounding of v[17] remains
+    assert np.abs(o[0] - v[17]).max() < 1e-15
+    # Scale enters as exp(scale * q.k): scores scaled by 1/2 equal keys halved.
+    q = rng.standard_normal((2, D)); k = rng.standard_normal((9, D)); v = rng.standard_normal((9, D))
+    assert np.abs(orc.attention_rows(q, k, v, 0.5) - orc.attention_rows(q, 0.5 * k, v, 1.0)).max() < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Decimal brute force
+# --------------------------------------------------------------------------
+def _decimal_attention(q, k, v, scale):
+    """Sum_t exp(s_t) v_t / Sum_t exp(s_t) and ln Sum_t exp(s_t) at 50 digits,
+    with no max subtraction (exact arithmetic needs none)."""
+    getcontext().prec = 50
+    R, D = q.shape
+    L = k.shape[0]
+    sc = Decimal(repr(float(scale)))
+    outs, lses = [], []
+    for r in range(R):
+        ws = []
+        for t in range(L):
+            dot = sum(Decimal(repr(float(q[r, d]))) * Decimal(repr(float(k[t, d]))) for d in range(D))
+            ws.append((sc * dot).exp())
+        tot = sum(ws)
+        outs.append([float(sum(ws[t] * Decimal(repr(float(v[t, d]))) for t in range(L)) / tot)
+                     for d in range(D)])
+        lses.append(float(tot.ln()))
+    return np.array(outs), np.array(lses)
+
+
+def pin_decimal_bruteforce(orc):
+    rng = _rng(2)
+    for trial in range(6):
+        R = int(rng.integers(1, 4))
+        L = int(rng.integers(1, 13))
+        D = int(rng.integers(1, 5))
+        q = rng.standard_normal((R, D)) * 2
+        k = rng.standard_normal((L, D)) * 2
+        v = rng.standard_normal((L, D))
+        scale = float(rng.uniform(0.2, 1.5))
+        ref_o, ref_lse = _decimal_attention(q, k, v, scale)
+        o = orc.attention_rows(q, k, v, scale)
+        assert np.abs(o - ref_o).max() < 1e-13, ("direct", trial)
+        for ns in range(1, L + 1):
+            op, lse = orc.split_partials_rows(q, k, v, ns, scale)
+            for s, (a, e) in enumerate(orc.split_bounds(L, ns)):
+                so, sl = _decimal_attention(q, k[a:e], v[a:e], scale)
+                assert np.abs(op[:, s, :] - so).max() < 1e-13, ("part", trial, ns, s)
+                assert np.abs(lse[s] - sl).max() < 1e-13, ("lse", trial, ns, s)
+            om = orc.merge_partials(op, lse)
+            assert np.abs(om - ref_o).max() < 1e-13, ("merge", trial, ns)
+
+
+# --------------------------------------------------------------------------
+# library cross-check: torch float64 scaled_dot_product_attention
+# --------------------------------------------------------------------------
+def _sdpa(q, k, v, scale, group):
+    """q [B,H,D], k/v [B,Hkv,L,D] -> [B,H,D] via torch SDPA in float64, with
+    K/V head j repeated for query heads j*G..j*G+G-1."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))[:, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64)).repeat_interleave(group, dim=1)
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64)).repeat_interleave(group, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o[:, :, 0, :].numpy()
+
+
+def pin_torch_sdpa(orc):
+    rng = _rng(3)
+    for (B, H, Hkv, D, L, ns) in [(2, 4, 4, 64, 256, 4), (1, 8, 1, 128, 300, 7),
+                                  (3, 28, 4, 32, 97, 8), (2, 32, 8, 16, 64, 64)]:
+        q = rng.standard_normal((B, H, D))
+        kb = rng.standard_normal((B, Hkv, L, D))
+        vb = rng.standard_normal((B, Hkv, L, D))
+        cu = [b * L for b in range(B + 1)]
+        scale = 1.0 / math.sqrt(D)
+        ref = _sdpa(q, kb, vb, scale, H // Hkv)
+        o_d = orc.attention_direct(q, kb, vb, cu, H, Hkv, scale, layout="bhsd")
+        o_s = orc.attention_split_merge(q, kb, vb, cu, H, Hkv, ns, scale, layout="bhsd")
+        assert np.abs(o_d - ref).max() < 1e-12, ("direct vs sdpa", B, H, Hkv, D)
+        assert np.abs(o_s - ref).max() < 1e-12, ("split vs sdpa", B, H, Hkv, D)
+        # Same data in the packed varlen layout [total, Hkv, D].
+        kp = kb.transpose(0, 2, 1, 3).reshape(B * L, Hkv, D)
+        vp = vb.transpose(0, 2, 1, 3).reshape(B * L, Hkv, D)
+        o_p = orc.attention_split_merge(q, kp, vp, cu, H, Hkv, ns, scale, layout="packed")
+        assert np.abs(o_p - ref).max() < 1e-12, ("packed vs sdpa", B, H, Hkv, D)
+    # Varlen: each packed sequence equals SDPA on that sequence alone.
+    lens = [5, 64, 1, 33]
+    H, Hkv, D = 6, 2, 16
+    q = rng.standard_normal((len(lens), H, D))
+    tot = sum(lens)
+    kp = rng.standard_normal((tot, Hkv, D)); vp = rng.standard_normal((tot, Hkv, D))
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    o = orc.attention_split_merge(q, kp, vp, cu, H, Hkv, 1, 0.4, layout="packed")
+    for b, L in enumerate(lens):
+        a = cu[b]
+        ks = kp[a:a + L].transpose(1, 0, 2)[None]
+        vs = vp[a:a + L].transpose(1, 0, 2)[None]
+        ref = _sdpa(q[b:b + 1], ks, vs, 0.4, H // Hkv)
+        assert np.abs(o[b:b + 1] - ref).max() < 1e-12, ("varlen seq", b)
+
+
+# --------------------------------------------------------------------------
+# invariant: split + merge equals direct (04_flash_decoding.py, demo 1)
+# --------------------------------------------------------------------------
+def pin_split_invariant(orc, splits=(1, 7, 64, 1000)):
+    """S = 10,000 keys, d = 128, R in {1, 8} packed query rows,
+    ns in {1, 7, 64, 1000}: the merged result equals direct attention to
+    1e-12 (demo 1 asserts exactness down to 10 keys per split)."""
+    rng = np.random.default_rng(0)
+    S, d = 10000, 128
+    for R in (1, 8):
+        q = rng.standard_normal((R, d))
+        K, V = rng.standard_normal((S, d)), rng.standard_normal((S, d))
+        scale = 1.0 / math.sqrt(d)
+        ref = orc.attention_rows(q, K, V, scale)
+        for ns in splits:
+            op, lse = orc.split_partials_rows(q, K, V, ns, scale)
+            o = orc.merge_partials(op, lse)
+            assert np.abs(o - ref).max() <= 1e-12, (R, ns, np.abs(o - ref).max())
+            # the per-split LSEs must also merge to the direct LSE
+            s = scale * (q @ K.T)
+            m = s.max(axis=1)
+            direct_lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+            mx = lse.max(axis=0)
+            merged = mx + np.log(np.exp(lse - mx).sum(axis=0))
+            assert np.abs(merged - direct_lse).max() <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# metamorphic relations
+# --------------------------------------------------------------------------
+def pin_metamorphic(orc):
+    rng = _rng(4)
+    # GQA equals MHA with each KV head repeated G times (query head h reads
+    # KV head h // G).
+    B, H, Hkv, D, L = 2, 12, 3, 8, 40
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B * L, Hkv, D)); v = rng.standard_normal((B * L, Hkv, D))
+    cu = [0, L, 2 * L]
+    G = H // Hkv
+    o_gqa = orc.attention_split_merge(q, k, v, cu, H, Hkv, 3, 0.35)
+    o_mha = orc.attention_split_merge(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1),
+                                      cu, H, H, 3, 0.35)
+    assert np.abs(o_gqa - o_mha).max() < 1e-14
+    # The KV head for query head h is h // G: moving head h's query to a head
+    # of another group changes its result unless the groups' K/V are equal.
+    o_alt = orc.attention_direct(q, k, v, cu, H, Hkv, 0.35)
+    for h in range(H):
+        j = h // G
+        ref = orc.attention_rows(q[:, h, :][0:1], k[0:L, j, :], v[0:L, j, :], 0.35)
+        assert np.abs(o_alt[0, h] - ref[0]).max() < 1e-14
+    # Permuting (k, v) pairs within a sequence leaves the output unchanged.
+    perm = rng.permutation(L)
+    kp = k.copy(); vp = v.copy()
+    kp[0:L] = k[0:L][perm]; vp[0:L] = v[0:L][perm]
+    o1 = orc.attention_direct(q, k, v, cu, H, Hkv, 0.35)
+    o2 = orc.attention_direct(q, kp, vp, cu, H, Hkv, 0.35)
+    assert np.abs(o1 - o2).max() < 1e-14
+    # A sequence inside a varlen batch equals the same sequence run alone.
+    lens = [3, 17, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    q = rng.standard_normal((3, H, D))
+    k = rng.standard_normal((sum(lens), Hkv, D)); v = rng.standard_normal((sum(lens), Hkv, D))
+    o = orc.attention_split_merge(q, k, v, cu, H, Hkv, 3, 0.5)
+    for b in range(3):
+        a, e = cu[b], cu[b + 1]
+        ob = orc.attention_split_merge(q[b:b + 1], k[a:e], v[a:e], [0, e - a], H, Hkv, 3, 0.5)
+        assert np.abs(o[b] - ob[0]).max() < 1e-14
+    # Shifting all scores of a split by a constant (adding c to every key
+    # along q) leaves o_s unchanged and shifts lse_s by scale * c * |q|^2-like
+    # term: here q = e0 and keys get +c in channel 0.
+    qq = np.zeros((1, D)); qq[0, 0] = 1.0
+    kk = rng.standard_normal((20, D)); vv = rng.standard_normal((20, D))
+    op1, l1 = orc.split_partials_rows(qq, kk, vv, 4, 0.5)
+    kk2 = kk.copy(); kk2[:, 0] += 3.0
+    op2, l2 = orc.split_partials_rows(qq, kk2, vv, 4, 0.5)
+    assert np.abs(op1 - op2).max() < 1e-13
+    assert np.abs((l2 - l1) - 1.5).max() < 1e-13
+
+
+ALL_PINS = [pin_split_bounds, pin_closed_forms, pin_decimal_bruteforce, pin_torch_sdpa,
+            pin_split_invariant, pin_metamorphic]

@@ -1,0 +1,10 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)

@@ -1,0 +1,131 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each mutant replaces one function of the oracle module for the duration of
+the test (the module's own internal calls see the replacement too) with a
+plausible slip: a wrong index, a dropped term, a transposed operand, the
+other split rule. The pins in ``oracle_pins`` must reject every one of them;
+a mutant that survives would mean the pins cannot tell that slip from the
+definition.
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as A
+from tests import oracle_pins as pins
+
+_orig = {n: getattr(A, n) for n in ("split_bounds", "kv_rows", "attention_rows",
+                                     "split_partials_rows", "merge_partials", "head_pairs")}
+
+
+def _bounds_ceil_equal(seqlen, num_splits):
+    # the other split rule (size = ceil(L/ns), start = s*size): can be empty
+    size = -(-seqlen // num_splits)
+    if num_splits < 1:
+        raise ValueError
+    return [(min(s * size, seqlen), min(s * size + size, seqlen)) for s in range(num_splits)]
+
+
+def _bounds_off_by_one(seqlen, num_splits):
+    b = _orig["split_bounds"](seqlen, num_splits)
+    return [(a, min(e + 1, seqlen)) for a, e in b]
+
+
+def _heads_modulo(heads, kv_heads):
+    # query head h -> KV head h % kv_heads instead of h // G
+    g = heads // kv_heads
+    return [(j, [h for h in range(heads) if h % kv_heads == j]) for j in range(kv_heads)] if g else []
+
+
+def _kv_rows_drop_last(kv, cu, b, kvh, layout):
+    return _orig["kv_rows"](kv, cu, b, kvh, layout)[:-1] if int(cu[b + 1]) - int(cu[b]) > 1 \
+        else _orig["kv_rows"](kv, cu, b, kvh, layout)
+
+
+def _kv_rows_next_seq(kv, cu, b, kvh, layout):
+    # reads the rows one position late (off-by-one varlen base)
+    start, end = int(cu[b]) + 1, int(cu[b + 1]) + 1
+    if layout == "packed":
+        r = kv[start:end, kvh, :]
+        if r.shape[0] < end - start:
+            r = kv[start - 1:end - 1, kvh, :]
+        return np.asarray(r, dtype=np.float64)
+    return np.asarray(kv[b, kvh, 1:end - start + 1, :], dtype=np.float64)
+
+
+def _rows_scale_squared(q, k, v, scale):
+    return _orig["attention_rows"](q, k, v, scale * scale)
+
+
+def _rows_kv_swapped(q, k, v, scale):
+    return _orig["attention_rows"](q, v, k, scale)
+
+
+def _partials_lse_no_max(q, k, v, ns, scale):
+    op, lse = _orig["split_partials_rows"](q, k, v, ns, scale)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    for s, (a, e) in enumerate(A.split_bounds(k.shape[0], ns)):
+        sc = scale * (q @ k[a:e].T)
+        m = sc.max(axis=1)
+        lse[s] = lse[s] - m            # forgot to add the max back
+    return op, lse
+
+
+def _partials_unnormalised(q, k, v, ns, scale):
+    op, lse = _orig["split_partials_rows"](q, k, v, ns, scale)
+    k = np.asarray(k, dtype=np.float64)
+    for s, (a, e) in enumerate(A.split_bounds(k.shape[0], ns)):
+        op[:, s, :] *= (e - a)         # sum instead of mean-like normalisation
+    return op, lse
+
+
+def _merge_no_normaliser(o_parts, lse):
+    lse = np.asarray(lse, dtype=np.float64)
+    w = np.exp(lse - lse.max(axis=0))  # weights not divided by their sum
+    return np.einsum("sr,rsd->rd", w, np.asarray(o_parts, dtype=np.float64))
+
+
+def _merge_uniform(o_parts, lse):
+    return np.asarray(o_parts, dtype=np.float64).mean(axis=1)
+
+
+def _merge_weight_by_dim(o_parts, lse):
+    # weight indexed by the wrong axis: every row gets row 0's weights
+    lse = np.asarray(lse, dtype=np.float64)
+    mx = lse.max(axis=0)
+    total = mx + np.log(np.exp(lse - mx).sum(axis=0))
+    w = np.exp(lse - total)
+    w = np.repeat(w[:, :1], w.shape[1], axis=1)
+    return np.einsum("sr,rsd->rd", w, np.asarray(o_parts, dtype=np.float64))
+
+
+MUTANTS = {
+    "bounds_ceil_equal": ("split_bounds", _bounds_ceil_equal),
+    "bounds_off_by_one": ("split_bounds", _bounds_off_by_one),
+    "heads_modulo": ("head_pairs", _heads_modulo),
+    "kv_rows_drop_last": ("kv_rows", _kv_rows_drop_last),
+    "kv_rows_shifted": ("kv_rows", _kv_rows_next_seq),
+    "scale_squared": ("attention_rows", _rows_scale_squared),
+    "kv_swapped": ("attention_rows", _rows_kv_swapped),
+    "lse_no_max": ("split_partials_rows", _partials_lse_no_max),
+    "partials_unnormalised": ("split_partials_rows", _partials_unnormalised),
+    "merge_no_normaliser": ("merge_partials", _merge_no_normaliser),
+    "merge_uniform": ("merge_partials", _merge_uniform),
+    "merge_weight_wrong_row": ("merge_partials", _merge_weight_by_dim),
+}
+
+# cheapest pins first; the test stops at the first one that rejects the mutant
+_ORDER = [pins.pin_closed_forms, pins.pin_metamorphic, pins.pin_split_bounds,
+          pins.pin_torch_sdpa, pins.pin_decimal_bruteforce, pins.pin_split_invariant]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    for pin in _ORDER:
+        try:
+            pin(A)
+        except Exception:
+            return
+    pytest.fail(f"mutant {name} passed every pin")
