@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of split-KV decode attention (libfd) on one MI355X.
+
+One step = one fd_decode_attention call (split kernel + LSE combine) over one
+batch of the workload, with every input already resident in HBM. The
+default workload is MHA decode at batch 4, 32 heads, 4096 keys, head dim 128,
+fp16, [batch, heads, seqlen, dim] layout, 16 splits. Several copies of K/V
+are rotated so that the 256 MB last-level cache never holds the next step's
+KV: every step streams its KV from HBM.
+
+Prints ONE JSON line: metric/value (achieved GB/s on the KV bytes of one
+step), ms_per_step, the roofline of the dominant kernel (the split kernel,
+timed by HIP events on the stream it runs on) and the CPU oracle's rate on
+the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/call + achieved HBM GB/s (fraction of ~8 TB/s) on 1 MI355X"
+PEAK_GBS = 8000.0
+LLC_BYTES = 256 * 2 ** 20       # MI355X Infinity Cache (MALL)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["fd_split.h", "fd_internal.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_09_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_by_name(name: str):
+    import workloads as W
+    for w in W.all_workloads():
+        if w.name == name:
+            return w
+    raise SystemExit(f"unknown workload {name!r}; known: "
+                     + ", ".join(w.name for w in W.all_workloads()))
+
+
+def pick_splits(w, lengths):
+    import workloads as W
+    import decode_attention_09_amd as fd
+    if w.num_splits is not None:
+        return W.varlen_splits(w, lengths) if w.varlen_range else w.num_splits
+    code = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}[w.dtype]
+    return fd.fd_plan_splits(w.batch, w.heads, w.kv_heads, w.dim, code, lengths)
+
+
+def traffic_for(workload_name: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counter
+    runs, or None if absent, for another workload, or the kernel changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, ns, budget_s: float):
+    """The fp64 numpy oracle (split + merge) on the same workload, one
+    (sequence, KV head) unit at a time in order, repeated until its own
+    compute time reaches ~budget_s seconds; BLAS limited to one thread.
+    Host copies of the inputs are made outside the clock."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    w = inp.workload
+    q = inp.q.float().cpu().numpy()
+    cu = inp.cu_seqlens_k.cpu().tolist()
+    units = [(b, j) for b in range(w.batch) for j in range(w.kv_heads)]
+    G = w.group
+    bytes_per_key = w.dim * 2 * w.elem_bytes     # one K row + one V row
+    done_bytes = 0
+    n_units = 0
+    oracle_s = 0.0
+    with threadpool_limits(limits=1):
+        while oracle_s < budget_s:
+            b, j = units[n_units % len(units)]
+            L = cu[b + 1] - cu[b]
+            if w.layout == "packed":
+                kr = inp.k[cu[b]:cu[b + 1], j].float().cpu().numpy()
+                vr = inp.v[cu[b]:cu[b + 1], j].float().cpu().numpy()
+            else:
+                kr = inp.k[b, j, :L].float().cpu().numpy()
+                vr = inp.v[b, j, :L].float().cpu().numpy()
+            t1 = time.perf_counter()
+            if L > 0:
+                op, lse = oracle.split_partials_rows(q[b, j * G:(j + 1) * G], kr, vr,
+                                                     min(ns, L), w.sm_scale)
+                oracle.merge_partials(op, lse)
+            oracle_s += time.perf_counter() - t1
+            done_bytes += L * bytes_per_key
+            n_units += 1
+    return {
+        "value": round(done_bytes / oracle_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n_units} (sequence, KV head) units of this workload "
+                  f"({n_units / len(units):.2f} passes), fp64 split+merge, "
+                  f"{oracle_s:.1f} s of oracle time",
+    }
+
+
+def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES):
+    import torch
+    import workloads as W
+    import decode_attention_09_amd as fd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(w, dev, seed=0)
+    ns = pick_splits(w, inp.lengths)
+    kv_bytes = inp.kv_bytes
+    copies = max(1, min(16, math.ceil(copies_min_bytes / max(1, kv_bytes))))
+    ks = [inp.k] + [inp.k.clone() for _ in range(copies - 1)]
+    vs = [inp.v] + [inp.v.clone() for _ in range(copies - 1)]
+    out = torch.empty_like(inp.q)
+    B, Hq, D = w.batch, w.heads, w.dim
+    ws = torch.empty(max(1, fd.fd_workspace_bytes(B, Hq, D, ns)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        k, v = ks[i % copies], vs[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        if ns == 1:
+            fd.fd_decode_attention(inp.q, k, v, inp.cu_seqlens_k, 1, out=out, layout=w.layout,
+                                   stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            fd.fd_decode_split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
+                               stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            fd.fd_decode_combine(ws, B, Hq, D, ns, out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    split_avg = sum(split_ms) / len(split_ms)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (split_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, no model weights)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.dim, "kv_len_total": sum(inp.lengths),
+                   "layout": w.layout, "num_splits": ns, "kv_bytes": kv_bytes,
+                   "kv_copies_rotated": copies, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic_for(w.name), "kernel": "fd::split_kernel",
+                     "kernel_us": round(split_avg * 1e3, 3),
+                     "kernel_us_p10_p90": [round(split_ms[len(split_ms) // 10] * 1e3, 3),
+                                           round(split_ms[(9 * len(split_ms)) // 10] * 1e3, 3)],
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "wall_s_timed": round(wall, 4),
+    }
+    if cpu_s > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mha_b4_h32_l4096_d128_f16")
+    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this implementation runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    if args.all:
+        import workloads as W
+        for w in W.all_workloads():
+            r = run(w, args.steps, args.warmup, 0.0)
+            print(json.dumps(r), flush=True)
+            import torch
+            torch.cuda.empty_cache()
+        return
+    print(json.dumps(run(workload_by_name(args.workload), args.steps, args.warmup,
+                         args.cpu_seconds)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

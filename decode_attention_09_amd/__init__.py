@@ -1,0 +1,222 @@
+"""Python binding of libfd (split-KV decode attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfd.so``, reached through the C ABI of ``include/fd.h`` via
+ctypes. PyTorch provides device memory and the stream. The functions carry
+the C names. There is no fallback: if the library is missing or the call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FD_F32", "FD_F16", "FD_BF16", "FD_MAX_SPLITS", "FdError", "library_path", "load_library",
+    "fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
+    "fd_decode_combine", "fd_status_string", "fd_last_error", "kv_layout",
+]
+
+FD_F32, FD_F16, FD_BF16 = 0, 1, 2
+FD_MAX_SPLITS = 16384
+_STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
+           3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        lib = load_library()
+        msg = lib.fd_status_string(status).decode()
+        extra = lib.fd_last_error().decode() if status == 4 else ""
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({msg}) {extra}".strip())
+
+
+class FdKvLayout(ctypes.Structure):
+    _fields_ = [("batch_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64), ("cu_stride", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfd.so")
+
+
+def load_library():
+    """Load libfd.so (built by ``decode_attention_09_amd.build``); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                           "python -m decode_attention_09_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lay = ctypes.POINTER(FdKvLayout)
+    lib.fd_plan_splits.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), i32,
+                                   i32, ctypes.POINTER(ctypes.c_int)]
+    lib.fd_plan_splits.restype = i32
+    lib.fd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.fd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fd_decode_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                        i32, lay]
+    lib.fd_decode_attention.restype = i32
+    lib.fd_decode_split.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, lay]
+    lib.fd_decode_split.restype = i32
+    lib.fd_decode_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32]
+    lib.fd_decode_combine.restype = i32
+    lib.fd_status_string.argtypes = [i32]
+    lib.fd_status_string.restype = ctypes.c_char_p
+    lib.fd_last_error.argtypes = []
+    lib.fd_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FdError(status, where)
+
+
+def fd_status_string(status: int) -> str:
+    return load_library().fd_status_string(int(status)).decode()
+
+
+def fd_last_error() -> str:
+    return load_library().fd_last_error().decode()
+
+
+# ----------------------------------------------------------- marshalling --
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FD_F32, torch.float16: FD_F16, torch.bfloat16: FD_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def kv_layout(k, layout: str = "packed"):
+    """Strides (elements) of a K or V tensor for the C ABI.
+
+    "packed": k is [total_kv, kv_heads, dim]; "bhsd": k is
+    [batch, kv_heads, max_len, dim]. The last dim must be contiguous.
+    """
+    if k.stride(-1) != 1:
+        raise ValueError("the head dim of K/V must be contiguous")
+    if layout == "packed":
+        if k.dim() != 3:
+            raise ValueError("packed K/V must be [total_kv, kv_heads, dim]")
+        return FdKvLayout(0, k.stride(1), k.stride(0), k.stride(0))
+    if layout == "bhsd":
+        if k.dim() != 4:
+            raise ValueError("bhsd K/V must be [batch, kv_heads, max_len, dim]")
+        return FdKvLayout(k.stride(0), k.stride(1), k.stride(2), 0)
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def fd_plan_splits(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, seqlens,
+                   num_cus: int = 0, max_splits: int = 0) -> int:
+    lib = load_library()
+    lens = [int(x) for x in seqlens]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    out = ctypes.c_int(0)
+    _check(lib.fd_plan_splits(batch, heads, kv_heads, dim, dtype, arr, num_cus, max_splits,
+                              ctypes.byref(out)), "fd_plan_splits")
+    return out.value
+
+
+def fd_workspace_bytes(batch: int, heads: int, dim: int, num_splits: int) -> int:
+    return int(load_library().fd_workspace_bytes(batch, heads, dim, num_splits))
+
+
+def _sizes(q, k, cu):
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, heads, dim]")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    batch, heads, dim = q.shape
+    kv_heads = k.shape[1]
+    if cu.numel() != batch + 1:
+        raise ValueError("cu_seqlens_k must have batch + 1 entries")
+    return batch, heads, kv_heads, dim
+
+
+def _workspace(q, batch, heads, dim, num_splits, workspace):
+    import torch
+    need = fd_workspace_bytes(batch, heads, dim, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace too small: need {need} bytes")
+    return workspace
+
+
+def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
+                        out=None, workspace=None, layout: str = "packed", stream=None):
+    """out[b,h] = softmax(scale q[b,h].K_b^T) V_b through libfd's two launches."""
+    import torch
+    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    if out is None:
+        out = torch.empty_like(q)
+    if num_splits > 1:
+        workspace = _workspace(q, batch, heads, dim, num_splits, workspace)
+    lay = kv_layout(k, layout)
+    _check(load_library().fd_decode_attention(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
+        int(num_splits), float(scale), _ptr(out), _ptr(workspace), _stream(stream, q.device),
+        _dtype_code(q), ctypes.byref(lay)), "fd_decode_attention")
+    return out
+
+
+def fd_decode_split(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
+                    workspace=None, layout: str = "packed", stream=None):
+    """First launch only; returns the workspace (uint8 tensor)."""
+    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    workspace = _workspace(q, batch, heads, dim, num_splits, workspace)
+    lay = kv_layout(k, layout)
+    _check(load_library().fd_decode_split(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
+        int(num_splits), float(scale), _ptr(workspace), _stream(stream, q.device),
+        _dtype_code(q), ctypes.byref(lay)), "fd_decode_split")
+    return workspace
+
+
+def fd_decode_combine(workspace, batch: int, heads: int, dim: int, num_splits: int, out,
+                      stream=None):
+    """Second launch only: merge the workspace into out [batch, heads, dim]."""
+    _check(load_library().fd_decode_combine(
+        _ptr(workspace), batch, heads, dim, int(num_splits), _ptr(out),
+        _stream(stream, out.device), _dtype_code(out)), "fd_decode_combine")
+    return out
+
+
+def workspace_views(workspace, batch: int, heads: int, dim: int, num_splits: int):
+    """(Opart [B,H,ns,D], LSE [B,ns,H]) fp32 views of a workspace, per the
+    layout documented in include/fd.h."""
+    import torch
+    n_o = batch * heads * num_splits * dim
+    off = ((n_o * 4 + 255) // 256) * 256
+    flat = workspace.view(torch.uint8)
+    opart = flat[:n_o * 4].view(torch.float32).view(batch, heads, num_splits, dim)
+    lse = flat[off:off + batch * num_splits * heads * 4].view(torch.float32).view(
+        batch, num_splits, heads)
+    return opart, lse

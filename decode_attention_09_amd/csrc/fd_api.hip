@@ -1,0 +1,284 @@
+// Host side of libfd: argument checks, workspace layout, split planner and
+// kernel dispatch behind the C ABI declared in include/fd.h.
+//
+// Argument rules mirror the host checks of flash_decode_splitk in
+// "flash_decode_splitk.py" (MiniInfer) -- supported head dims, positive
+// sizes, heads a multiple of kv_heads, positive split count -- returned as
+// status codes instead of exceptions. The planner follows the split-count
+// guidance of "04_flash_decoding.py" (CS349E lecture 11), demo 4, the
+// 256-keys-per-split default of flash_decode_splitk.py, and the rule of
+// "decode_attention_splitkv.py" (TileLang tutorial, ch. 18) that no split may
+// be empty.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fd.h"
+#include "fd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
+                (int)e);
+  return FD_ERR_HIP;
+}
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr int64_t kMaxWorkgroups = int64_t(1) << 24;
+// Resident split workgroups per compute unit assumed by the planner (the
+// split kernel's 4-wave workgroups at its register footprint).
+constexpr int kPlanGroupsPerCu = 2;
+// Fewest keys per split the planner will create (flash_decode_splitk.py's
+// default of one split per 256 keys).
+constexpr int kPlanMinKeysPerSplit = 256;
+
+int elem_bytes(int dtype) { return dtype == FD_F32 ? 4 : 2; }
+
+bool dim_ok(int dim) { return dim == 16 || dim == 32 || dim == 64 || dim == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Sizes {
+  int group, rows, row_chunks;
+  int64_t workgroups;
+};
+
+// Checks shared by every launching entry point.
+int check_common(int batch, int heads, int kv_heads, int dim, int num_splits, int dtype,
+                 Sizes* sz) {
+  if (batch < 1 || heads < 1 || kv_heads < 1 || num_splits < 1) return FD_ERR_INVALID_ARG;
+  if (heads % kv_heads != 0) return FD_ERR_INVALID_ARG;
+  if (num_splits > FD_MAX_SPLITS) return FD_ERR_INVALID_ARG;
+  if (dtype != FD_F32 && dtype != FD_F16 && dtype != FD_BF16) return FD_ERR_UNSUPPORTED;
+  if (!dim_ok(dim)) return FD_ERR_UNSUPPORTED;
+  const int group = heads / kv_heads;
+  if (group > FD_MAX_GROUP) return FD_ERR_UNSUPPORTED;
+  sz->group = group;
+  sz->rows = group < fd::kMaxRowsPerPass ? group : fd::kMaxRowsPerPass;
+  sz->row_chunks = (group + fd::kMaxRowsPerPass - 1) / fd::kMaxRowsPerPass;
+  sz->workgroups = (int64_t)batch * kv_heads * sz->row_chunks * num_splits;
+  if (sz->workgroups > kMaxWorkgroups) return FD_ERR_INVALID_ARG;
+  if ((int64_t)batch * heads > INT_MAX / 2) return FD_ERR_INVALID_ARG;
+  return FD_OK;
+}
+
+int check_layout(const fd_kv_layout* lay, int kv_heads, int dim, int dtype, fd_kv_layout* out) {
+  fd_kv_layout L;
+  if (lay == nullptr) {
+    L.batch_stride = 0;
+    L.head_stride = dim;
+    L.token_stride = (int64_t)kv_heads * dim;
+    L.cu_stride = (int64_t)kv_heads * dim;
+  } else {
+    L = *lay;
+  }
+  if (L.batch_stride < 0 || L.head_stride < 0 || L.token_stride < dim || L.cu_stride < 0)
+    return FD_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t s[4] = {L.batch_stride, L.head_stride, L.token_stride, L.cu_stride};
+  for (int64_t x : s)
+    if ((x * eb) % 16 != 0) return FD_ERR_INVALID_ARG;
+  // Offsets inside one tile are 32-bit: keep a tile (<= 128 keys) far
+  // below 2^32 bytes.
+  if (L.token_stride * eb > (int64_t(1) << 23)) return FD_ERR_INVALID_ARG;
+  *out = L;
+  return FD_OK;
+}
+
+int launch_split(const void* q, const void* k, const void* v, const int32_t* cu, int batch,
+                 int heads, int kv_heads, int dim, int num_splits, float scale, float* opart,
+                 float* lse, void* out, int direct, hipStream_t stream, int dtype,
+                 const fd_kv_layout& L, const Sizes& sz) {
+  fd::SplitArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu = cu;
+  a.opart = opart;
+  a.lse = lse;
+  a.out = out;
+  a.sb = L.batch_stride;
+  a.sh = L.head_stride;
+  a.st = L.token_stride;
+  a.scu = L.cu_stride;
+  a.heads = heads;
+  a.kv_heads = kv_heads;
+  a.group = sz.group;
+  a.num_splits = num_splits;
+  a.row_chunks = sz.row_chunks;
+  a.direct = direct;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  dim3 grid((unsigned)sz.workgroups);
+  hipError_t e;
+  switch (dtype) {
+    case FD_F32: e = fd::launch_split_f32(a, dim, sz.rows, grid, stream); break;
+    case FD_F16: e = fd::launch_split_f16(a, dim, sz.rows, grid, stream); break;
+    default: e = fd::launch_split_bf16(a, dim, sz.rows, grid, stream); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  return FD_OK;
+}
+
+size_t opart_bytes(int batch, int heads, int dim, int num_splits) {
+  return (size_t)batch * heads * num_splits * dim * sizeof(float);
+}
+
+size_t lse_offset(int batch, int heads, int dim, int num_splits) {
+  return (opart_bytes(batch, heads, dim, num_splits) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits) {
+  if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS || !dim_ok(dim))
+    return 0;
+  const double est = (double)batch * heads * num_splits * (dim + 1) * 4.0;
+  if (est > 1e18) return 0;
+  return lse_offset(batch, heads, dim, num_splits) +
+         (size_t)batch * num_splits * heads * sizeof(float);
+}
+
+int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
+                   const int32_t* seqlens_host, int num_cus, int max_splits,
+                   int* num_splits_out) {
+  if (num_splits_out == nullptr || seqlens_host == nullptr) return FD_ERR_INVALID_ARG;
+  Sizes sz;
+  int st = check_common(batch, heads, kv_heads, dim, 1, dtype, &sz);
+  if (st != FD_OK) return st;
+  int64_t min_len = INT64_MAX, max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t x = seqlens_host[b];
+    if (x < min_len) min_len = x;
+    if (x > max_len) max_len = x;
+  }
+  if (min_len < 1) return FD_ERR_EMPTY_SPLIT;
+  if (num_cus < 0) return FD_ERR_INVALID_ARG;
+  if (num_cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
+  // candidate range: every split non-empty, the longest sequence keeps
+  // >= kPlanMinKeysPerSplit keys per split, workgroup count bounded
+  int64_t cap = (max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
+  if (cap > min_len) cap = min_len;
+  if (cap > max_splits) cap = max_splits;
+  const int64_t units = (int64_t)batch * kv_heads * sz.row_chunks;
+  while (cap > 1 && units * cap > kMaxWorkgroups) --cap;
+  if (cap < 1) cap = 1;
+  const int64_t slots = (int64_t)num_cus * kPlanGroupsPerCu;
+  // fill(ns): share of workgroup slots busy, averaged over the passes
+  // needed (wave quantisation); pick the smallest ns within 90% of the best.
+  double best = 0.0;
+  for (int64_t ns = 1; ns <= cap; ++ns) {
+    const int64_t wgs = units * ns;
+    const int64_t passes = (wgs + slots - 1) / slots;
+    const double fill = (double)wgs / (double)(passes * slots);
+    if (fill > best) best = fill;
+  }
+  int choice = 1;
+  for (int64_t ns = 1; ns <= cap; ++ns) {
+    const int64_t wgs = units * ns;
+    const int64_t passes = (wgs + slots - 1) / slots;
+    const double fill = (double)wgs / (double)(passes * slots);
+    if (fill >= 0.9 * best) {
+      choice = (int)ns;
+      break;
+    }
+  }
+  *num_splits_out = choice;
+  return FD_OK;
+}
+
+int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
+                    int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
+                    void* workspace, void* stream, int dtype, const fd_kv_layout* layout) {
+  Sizes sz;
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz);
+  if (st != FD_OK) return st;
+  if (!q || !k || !v || !cu_seqlens_k || !workspace) return FD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
+    return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  fd_kv_layout L;
+  st = check_layout(layout, kv_heads, dim, dtype, &L);
+  if (st != FD_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  float* opart = reinterpret_cast<float*>(ws);
+  float* lse = reinterpret_cast<float*>(ws + lse_offset(batch, heads, dim, num_splits));
+  return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
+                      opart, lse, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz);
+}
+
+int fd_decode_combine(const void* workspace, int batch, int heads, int dim, int num_splits,
+                      void* out, void* stream, int dtype) {
+  if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS)
+    return FD_ERR_INVALID_ARG;
+  if ((int64_t)batch * heads > INT_MAX / 2) return FD_ERR_INVALID_ARG;
+  if (dtype != FD_F32 && dtype != FD_F16 && dtype != FD_BF16) return FD_ERR_UNSUPPORTED;
+  if (!dim_ok(dim)) return FD_ERR_UNSUPPORTED;
+  if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  const char* ws = static_cast<const char*>(workspace);
+  fd::CombineArgs a;
+  a.opart = reinterpret_cast<const float*>(ws);
+  a.lse = reinterpret_cast<const float*>(ws + lse_offset(batch, heads, dim, num_splits));
+  a.out = out;
+  a.batch = batch;
+  a.heads = heads;
+  a.num_splits = num_splits;
+  hipError_t e = fd::launch_combine(a, dtype, dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return FD_OK;
+}
+
+int fd_decode_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
+                        int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
+                        void* out, void* workspace, void* stream, int dtype,
+                        const fd_kv_layout* layout) {
+  Sizes sz;
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz);
+  if (st != FD_OK) return st;
+  if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
+  if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  fd_kv_layout L;
+  st = check_layout(layout, kv_heads, dim, dtype, &L);
+  if (st != FD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_splits == 1) {
+    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, nullptr,
+                        nullptr, out, 1, s, dtype, L, sz);
+  }
+  st = fd_decode_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
+                       workspace, stream, dtype, layout);
+  if (st != FD_OK) return st;
+  return fd_decode_combine(workspace, batch, heads, dim, num_splits, out, stream, dtype);
+}
+
+const char* fd_status_string(int status) {
+  switch (status) {
+    case FD_OK: return "ok";
+    case FD_ERR_INVALID_ARG: return "invalid argument";
+    case FD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FD_ERR_EMPTY_SPLIT: return "a sequence has no key (empty split)";
+    case FD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fd_last_error(void) { return g_last_error; }
+
+}  // extern "C"

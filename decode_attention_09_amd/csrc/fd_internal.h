@@ -1,0 +1,44 @@
+// Internal declarations shared by the host layer and the kernel sources of
+// libfd. Not part of the public ABI (see include/fd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fd {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kWavesPerGroup = 4;  // waves per split workgroup
+constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
+constexpr int kLoadsPerTile = 4;   // 16-byte K (and V) loads per lane per tile
+
+// Arguments of the split kernel (passed by value).
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu;
+  float* opart;     // [B, H, ns, D] fp32 (workspace mode)
+  float* lse;       // [B, ns, H]   fp32 (workspace mode)
+  void* out;        // [B, H, D] dtype (direct mode, ns == 1)
+  int64_t sb, sh, st, scu;  // K/V strides in elements: batch, head, token, cu
+  int heads, kv_heads, group, num_splits, row_chunks;
+  int direct;       // 1: write out in dtype; 0: write opart/lse
+  float scale_log2; // scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* opart;
+  const float* lse;
+  void* out;
+  int batch, heads, num_splits;
+};
+
+// Launchers (defined in fd_split_<dtype>.hip and fd_combine.hip). They
+// return the hipError_t of the launch.
+hipError_t launch_split_f32(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
+hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
+hipError_t launch_split_bf16(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s);
+
+}  // namespace fd

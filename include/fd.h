@@ -1,0 +1,181 @@
+/*
+ * fd.h -- C ABI of libfd: single-query split-KV decode attention
+ * ("flash decoding") for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. For every sequence b and query head h of one decode
+ * step, with G = heads / kv_heads and KV head j = h / G:
+ *
+ *     o[b,h,:] = softmax_t( scale * q[b,h,:] . K[b,t,j,:] ) V[b,t,j,:],
+ *                t in [0, L_b),  L_b = cu_seqlens_k[b+1] - cu_seqlens_k[b].
+ *
+ * The KV axis of each (b, j) is cut into num_splits proportional segments
+ * [L_b*s/num_splits, L_b*(s+1)/num_splits) (integer division). A first
+ * kernel computes, per segment, the normalised partial output and its
+ * log-sum-exp, with the G query heads of a group packed so one read of a
+ * K/V row serves all of them; a second kernel merges the segments exactly
+ * with log-sum-exp weights.
+ *
+ * Sources:
+ *   - "decode_attention_splitkv.py" (TileLang tutorial, ch. 18):
+ *     gqa_decode_splitkv -- GQA packing, cu_seqlens_k varlen addressing,
+ *     proportional split bounds, split epilogue (o_s, base-2 LSE), combine
+ *     segment; its docstring's rule that every split must hold >= 1 key.
+ *   - "flash_decode_splitk.py" (MiniInfer): flash_decode_splitk host checks
+ *     (supported head dims, positive KV length, default scale 1/sqrt(dim),
+ *     default split count), output cast back to the input dtype.
+ *   - "04_flash_decoding.py" (CS349E lecture 11), demos 1 and 4: the exact
+ *     LSE merge, and choosing the split count so the number of workgroups is
+ *     one to a few times the number of compute units (wave quantisation).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers, owned by the caller, and must
+ *     be 16-byte aligned. The library allocates no device memory and keeps
+ *     no per-call state; calls are asynchronous on `stream` (a hipStream_t
+ *     passed as void*, NULL = the default stream) and never synchronise.
+ *   - Element type `dtype` (FD_F32, FD_F16, FD_BF16) applies to q, k, v and
+ *     out. Arithmetic is fp32 throughout; out is rounded to dtype
+ *     (round-to-nearest-even).
+ *   - Return value: FD_OK or an FD_ERR_* code. Argument checks run on the
+ *     host before anything is launched; a failed check launches nothing and
+ *     leaves every buffer untouched.
+ *   - cu_seqlens_k lives on the device and is never read by the host, so
+ *     the device path cannot check `num_splits <= L_b`. A split that holds
+ *     no key contributes nothing (its LSE is -inf, its partial output 0),
+ *     and a sequence with L_b = 0 yields an all-zero output row. Callers
+ *     should pick num_splits with fd_plan_splits, which enforces the rule.
+ */
+#ifndef FD_H_
+#define FD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v, out. */
+enum { FD_F32 = 0, FD_F16 = 1, FD_BF16 = 2 };
+
+/* Status codes. */
+enum {
+  FD_OK = 0,
+  FD_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or alignment */
+  FD_ERR_UNSUPPORTED = 2,  /* dim not in {16,32,64,128}, dtype, group > 64 */
+  FD_ERR_EMPTY_SPLIT = 3,  /* planner: some sequence has no key */
+  FD_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+};
+
+/* Limits. */
+#define FD_MAX_SPLITS 16384
+#define FD_MAX_GROUP 64
+
+/*
+ * Where the K/V row of sequence b, key t, KV head j starts, in elements:
+ *
+ *     b*batch_stride + cu_seqlens_k[b]*cu_stride + t*token_stride + j*head_stride
+ *
+ * Packed varlen [total_kv, kv_heads, dim] (decode_attention_splitkv.py,
+ * shape_kv):        {0, dim, kv_heads*dim, kv_heads*dim}
+ * Padded [batch, kv_heads, max_len, dim] (flash_decode_splitk.py's
+ * [batch, heads, seqlen, dim]): {kv_heads*max_len*dim, max_len*dim, dim, 0}
+ *
+ * Field order: batch_stride, head_stride, token_stride, cu_stride. All are
+ * >= 0, token_stride >= dim, and stride*element_size must be a multiple of
+ * 16 bytes. K and V share the layout. NULL means packed.
+ */
+typedef struct fd_kv_layout {
+  int64_t batch_stride;
+  int64_t head_stride;
+  int64_t token_stride;
+  int64_t cu_stride;
+} fd_kv_layout;
+
+/*
+ * fd_plan_splits -- choose num_splits for a batch (host only, no device
+ * access unless num_cus == 0).
+ *
+ *   seqlens_host  int32[batch] KV lengths on the host.
+ *   num_cus       compute units to plan for; 0 = query the current device.
+ *   max_splits    upper bound on the result (<= 0 means FD_MAX_SPLITS).
+ *   *num_splits_out  receives the choice.
+ *
+ * Rule (04_flash_decoding.py, demo 4; flash_decode_splitk.py's floor of
+ * 256 keys per split; decode_attention_splitkv.py's non-empty rule): among
+ * split counts that leave every split >= 1 key and the longest sequence
+ * >= 256 keys per split, take the smallest whose workgroup count fills the
+ * device's workgroup slots to within 90% of the best fill (wave
+ * quantisation), preferring no split when one pass already fills them.
+ * Returns FD_ERR_EMPTY_SPLIT if some length is < 1, FD_ERR_INVALID_ARG for
+ * bad sizes, FD_ERR_HIP if the device query fails.
+ */
+int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
+                   const int32_t* seqlens_host, int num_cus, int max_splits,
+                   int* num_splits_out);
+
+/*
+ * fd_workspace_bytes -- size of the fp32 workspace for a call with these
+ * sizes (0 on overflow or bad sizes). Layout, all fp32:
+ *   Opart [batch, heads, num_splits, dim]  normalised partial outputs o_s
+ *   LSE   [batch, num_splits, heads]       log2(sum_t 2^(s2_t)) of split s,
+ *                                           s2_t = scale*log2(e)*q.k_t
+ * LSE starts at the first 256-byte boundary after Opart. The shapes follow
+ * part_shape / lse_shape of decode_attention_splitkv.py, in fp32.
+ */
+size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits);
+
+/*
+ * fd_decode_attention -- the whole hot path: split kernel + LSE combine.
+ *
+ *   q             [batch, heads, dim] dtype, contiguous.
+ *   k, v          KV cache, addressed by `layout` (NULL = packed).
+ *   cu_seqlens_k  int32[batch+1] device array of non-decreasing offsets.
+ *   num_splits    1..FD_MAX_SPLITS. With 1, the split kernel writes `out`
+ *                 directly and `workspace` may be NULL.
+ *   scale         softmax scale on q.k in natural-exp units (any finite
+ *                 value; 1/sqrt(dim) is the usual choice).
+ *   out           [batch, heads, dim] dtype, fully overwritten.
+ *   workspace     fd_workspace_bytes(...) bytes of device memory, or NULL
+ *                 when num_splits == 1. Contents on return: the partials.
+ *   stream        hipStream_t as void*.
+ */
+int fd_decode_attention(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_k, int batch, int heads,
+                        int kv_heads, int dim, int num_splits, float scale,
+                        void* out, void* workspace, void* stream, int dtype,
+                        const fd_kv_layout* layout);
+
+/*
+ * fd_decode_split -- first launch only: writes Opart and LSE for every
+ * (b, h, split) into `workspace` (required, for any num_splits >= 1).
+ * Same arguments as fd_decode_attention minus `out`.
+ */
+int fd_decode_split(const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_k, int batch, int heads,
+                    int kv_heads, int dim, int num_splits, float scale,
+                    void* workspace, void* stream, int dtype,
+                    const fd_kv_layout* layout);
+
+/*
+ * fd_decode_combine -- second launch only: merges the Opart/LSE workspace
+ * written by fd_decode_split (or any producer of the same layout, e.g. the
+ * shards of a sequence-parallel split) into out [batch, heads, dim] dtype:
+ * M = max_s LSE_s, lse = M + log2 sum_s 2^(LSE_s - M),
+ * out = sum_s 2^(LSE_s - lse) * Opart_s (combine segment of
+ * decode_attention_splitkv.py). Rows whose splits are all empty get 0.
+ */
+int fd_decode_combine(const void* workspace, int batch, int heads, int dim,
+                      int num_splits, void* out, void* stream, int dtype);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fd_status_string(int status);
+
+/* Last HIP error text recorded by this thread when FD_ERR_HIP was returned
+ * (static per-thread buffer, "" if none). */
+const char* fd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H_ */

@@ -1,0 +1,102 @@
+"""Shared helpers of the GPU parity tests: run libfd on seeded inputs and
+compare with the fp64 oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+# Max-abs error allowed against the fp64 oracle, per input dtype.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+LOG2E = 1.0 / math.log(2.0)
+DEV = "cuda:0"
+
+
+def fd():
+    import decode_attention_09_amd as m
+    return m
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU (run with -m 'not gpu' on CPU)"
+    fd().load_library()
+
+
+def announce(*parts):
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 host copy (fp16/bf16 values are exactly representable)."""
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def gpu_attention(inp: W.Inputs, ns: int, scale=None, stream=None):
+    w = inp.workload
+    announce("fd_decode_attention", w.name, f"ns={ns}", f"lens[:4]={inp.lengths[:4]}")
+    out = fd().fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns,
+                                   scale=w.sm_scale if scale is None else scale,
+                                   layout=w.layout, stream=stream)
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_split(inp: W.Inputs, ns: int, scale=None):
+    w = inp.workload
+    announce("fd_decode_split", w.name, f"ns={ns}")
+    ws = fd().fd_decode_split(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns,
+                              scale=w.sm_scale if scale is None else scale, layout=w.layout)
+    torch.cuda.synchronize()
+    opart, lse = fd().workspace_views(ws, w.batch, w.heads, w.dim, ns)
+    return ws, host(opart), host(lse)
+
+
+def oracle_full(inp: W.Inputs, ns: int | None = None, scale=None):
+    """Oracle output for the whole batch (split+merge when ns is valid for
+    every sequence, direct otherwise)."""
+    w = inp.workload
+    q, k, v = host(inp.q), host(inp.k), host(inp.v)
+    cu = inp.cu_seqlens_k.cpu().tolist()
+    sc = w.sm_scale if scale is None else scale
+    if ns is not None and min(inp.lengths) >= ns:
+        return oracle.attention_split_merge(q, k, v, cu, w.heads, w.kv_heads, ns, sc,
+                                            layout=w.layout)
+    return oracle.attention_direct(q, k, v, cu, w.heads, w.kv_heads, sc, layout=w.layout)
+
+
+def oracle_pairs(inp: W.Inputs, pairs, scale=None):
+    """Oracle rows for a few (b, kv_head) pairs, copying only their K/V rows
+    to the host. Returns {(b, kvh): o [G, D]}."""
+    w = inp.workload
+    G = w.group
+    sc = w.sm_scale if scale is None else scale
+    cu = inp.cu_seqlens_k.cpu().tolist()
+    res = {}
+    for b, j in pairs:
+        L = cu[b + 1] - cu[b]
+        if w.layout == "packed":
+            kr = host(inp.k[cu[b]:cu[b + 1], j, :])
+            vr = host(inp.v[cu[b]:cu[b + 1], j, :])
+        else:
+            kr = host(inp.k[b, j, :L, :])
+            vr = host(inp.v[b, j, :L, :])
+        qr = host(inp.q[b, j * G:(j + 1) * G, :])
+        res[(b, j)] = oracle.attention_rows(qr, kr, vr, sc)
+    return res
+
+
+def max_err(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if a.size == 0:
+        return 0.0
+    d = np.abs(a - b)
+    assert np.isfinite(d).all(), "non-finite values in the comparison"
+    return float(d.max())

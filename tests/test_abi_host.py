@@ -1,0 +1,172 @@
+"""Host-side tests of libfd (no GPU needed): the shared library loads, exports
+every function include/fd.h declares, sizes its workspace as documented,
+plans split counts by its stated rule, and rejects bad arguments before
+launching anything."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+fd = pytest.importorskip("decode_attention_09_amd")
+
+
+def _lib():
+    try:
+        return fd.load_library()
+    except RuntimeError as e:  # pragma: no cover - only when not built
+        pytest.fail(f"libfd.so must be built before the tests: {e}")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
+              "fd_decode_combine", "fd_status_string", "fd_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_python_binding_has_the_c_names():
+    for n in declared_functions():
+        assert callable(getattr(fd, n)), n
+
+
+def test_status_strings():
+    assert fd.fd_status_string(0) == "ok"
+    for s in (1, 2, 3, 4, 99):
+        assert isinstance(fd.fd_status_string(s), str) and fd.fd_status_string(s)
+    assert fd.fd_last_error() == ""
+
+
+@pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (32, 28, 128, 8),
+                                      (3, 5, 64, 1000)])
+def test_workspace_bytes_layout(B, H, D, ns):
+    n = fd.fd_workspace_bytes(B, H, D, ns)
+    opart = B * H * ns * D * 4
+    lse_off = (opart + 255) // 256 * 256
+    assert n == lse_off + B * ns * H * 4
+
+
+def test_workspace_bytes_rejects_bad_sizes():
+    assert fd.fd_workspace_bytes(0, 8, 128, 4) == 0
+    assert fd.fd_workspace_bytes(1, 8, 100, 4) == 0
+    assert fd.fd_workspace_bytes(1, 8, 128, 0) == 0
+    assert fd.fd_workspace_bytes(1, 8, 128, fd.FD_MAX_SPLITS + 1) == 0
+
+
+# ----------------------------------------------------------------- planner --
+def plan(B, H, Hkv, D, lens, cus=256, max_splits=0, dtype=fd.FD_F16):
+    return fd.fd_plan_splits(B, H, Hkv, D, dtype, lens, cus, max_splits)
+
+
+def test_planner_never_creates_an_empty_split():
+    # decode_attention_splitkv.py: every split needs >= 1 key, else fall back
+    for lens in ([1], [3, 4096], [7, 100000], [64] * 32, [1, 1, 1]):
+        ns = plan(len(lens), 8, 1, 128, lens)
+        assert 1 <= ns <= min(lens)
+
+
+def test_planner_rejects_empty_sequences():
+    with pytest.raises(fd.FdError) as e:
+        plan(2, 8, 1, 128, [5, 0])
+    assert e.value.status == 3
+
+
+def test_planner_keeps_256_keys_per_split():
+    for L in (256, 1000, 4096, 65536, 131072):
+        ns = plan(1, 32, 8, 128, [L])
+        assert ns <= max(1, math.ceil(L / 256))
+
+
+def test_planner_no_split_when_one_pass_fills_the_device():
+    # 256 x 2 KV heads = 512 workgroups fill 256 CUs x 2 slots in one pass
+    assert plan(256, 16, 2, 128, [256] * 256) == 1
+
+
+def test_planner_splits_a_single_long_sequence():
+    # 1 sequence x 8 KV heads: one workgroup per head leaves the device idle
+    ns = plan(1, 32, 8, 128, [131072])
+    wgs = 8 * ns
+    assert ns > 16 and wgs <= 2 * 256 and wgs >= 0.9 * 512
+
+
+def test_planner_wave_quantisation_example():
+    # 04_flash_decoding.py, demo 4: batch 64, S=2K, 16/2 heads on 108 SMs;
+    # without splitting, 128 CTAs leave the second wave nearly empty, while
+    # 4-16 splits pack the waves. With one resident workgroup per SM:
+    ns = fd.fd_plan_splits(64, 16, 2, 128, fd.FD_F16, [2048] * 64, 54, 0)
+    # (54 CUs x 2 slots = 108 slots, the same slot count as the page's 108 SMs)
+    assert 2 <= ns <= 16
+    wgs = 128 * ns
+    passes = math.ceil(wgs / 108)
+    assert wgs / (passes * 108) > 128 / (2 * 108)
+
+
+def test_planner_respects_max_splits():
+    assert plan(1, 32, 8, 128, [131072], max_splits=4) <= 4
+
+
+def test_planner_argument_errors():
+    with pytest.raises(fd.FdError):
+        plan(1, 30, 8, 128, [100])           # heads not a multiple of kv_heads
+    with pytest.raises(fd.FdError) as e:
+        plan(1, 32, 8, 100, [100])           # unsupported head dim
+    assert e.value.status == 2
+    with pytest.raises(fd.FdError):
+        plan(0, 32, 8, 128, [])
+
+
+# ---------------------------------------------------- argument rejection --
+def _attn(lib, **kw):
+    base = dict(q=16, k=16, v=16, cu=16, B=1, H=8, Hkv=1, D=128, ns=2, scale=0.1, out=16,
+                ws=16, stream=None, dt=fd.FD_F16, lay=None)
+    base.update(kw)
+    return lib.fd_decode_attention(base["q"], base["k"], base["v"], base["cu"], base["B"],
+                                   base["H"], base["Hkv"], base["D"], base["ns"],
+                                   base["scale"], base["out"], base["ws"], base["stream"],
+                                   base["dt"], base["lay"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(cu=None), 1), (dict(out=None), 1),
+    (dict(ws=None), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(H=9, Hkv=2), 1),
+    (dict(ns=0), 1), (dict(ns=fd.FD_MAX_SPLITS + 1), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(q=8), 1), (dict(D=96), 2), (dict(D=256), 2),
+    (dict(dt=7), 2), (dict(H=65, Hkv=1), 2),
+])
+def test_decode_attention_rejects_before_launch(kw, status):
+    assert _attn(_lib(), **kw) == status
+
+
+def test_layout_checks():
+    lib = _lib()
+    bad = [fd.FdKvLayout(0, 128, 64, 0),      # token stride < dim
+           fd.FdKvLayout(-1, 128, 128, 0),    # negative stride
+           fd.FdKvLayout(0, 100, 128, 128),   # head stride not 16-byte aligned (fp16)
+           fd.FdKvLayout(0, 128, 1 << 23, 0)]  # tile offsets would not fit 32 bits
+    for lay in bad:
+        assert _attn(lib, lay=ctypes.byref(lay)) == 1
+
+
+def test_split_and_combine_reject_before_launch():
+    lib = _lib()
+    assert lib.fd_decode_split(16, 16, 16, 16, 1, 8, 1, 128, 2, 0.1, None, None, 1, None) == 1
+    assert lib.fd_decode_combine(None, 1, 8, 128, 2, 16, None, 1) == 1
+    assert lib.fd_decode_combine(16, 1, 8, 128, 2, None, None, 1) == 1
+    assert lib.fd_decode_combine(16, 1, 8, 96, 2, 16, None, 1) == 2
+    assert lib.fd_decode_combine(16, 0, 8, 128, 2, 16, None, 1) == 1

@@ -1,0 +1,232 @@
+"""GPU tests with exact answers: split boundaries and varlen indexing made
+bit-exactly observable, edge cases, and a grid of head dims x dtypes x group
+sizes with ragged tiles against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    H.require_gpu()
+    yield
+
+
+def _bounds(L, ns):
+    """Proportional bounds, including the empty splits that ns > L gives
+    (the oracle raises there; the library documents LSE=-inf, o=0)."""
+    if L >= ns >= 1:
+        return oracle.split_bounds(L, ns)
+    return [(L * s // ns, L * (s + 1) // ns) for s in range(ns)]
+
+
+def structured_inputs(lengths, heads, kv_heads, dim, dtype, ns, layout, pad=3):
+    """K = 0 so every score is 0 and every key weighs exactly 1. V carries
+    integers: channel 0 is 1 at each split's first key, channel 1 is 1 at its
+    last key, channel 2 is the sequence index, channel 3 the KV head index,
+    channel 4 the key position mod 16. Rows outside every sequence are NaN."""
+    B = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(cu[-1])
+    rng = np.random.default_rng(7)
+    q = torch.from_numpy(rng.standard_normal((B, heads, dim)).astype(np.float32)).to(DT[dtype])
+    if layout == "packed":
+        k = torch.full((T + pad, kv_heads, dim), float("nan"))
+        v = torch.full((T + pad, kv_heads, dim), float("nan"))
+        k[:T] = 0
+        v[:T] = 0
+    else:
+        S = max(lengths)
+        k = torch.full((B, kv_heads, S + pad, dim), float("nan"))
+        v = torch.full((B, kv_heads, S + pad, dim), float("nan"))
+    for b, L in enumerate(lengths):
+        for j in range(kv_heads):
+            if layout == "packed":
+                rows = v[int(cu[b]):int(cu[b]) + L, j]
+            else:
+                k[b, j, :L] = 0
+                v[b, j, :L] = 0
+                rows = v[b, j, :L]
+            rows[:, 2] = b
+            rows[:, 3] = j
+            rows[:, 4] = torch.arange(L) % 16
+            for a, e in _bounds(L, ns):
+                if e > a:
+                    rows[a, 0] = 1
+                    rows[e - 1, 1] = 1
+    w = W.Workload("structured", B, heads, kv_heads, dim, dtype, kv_len=None, layout=layout,
+                   num_splits=ns)
+    cu_t = torch.tensor(cu, dtype=torch.int32)
+    return W.Inputs(w, q.to(H.DEV), k.to(DT[dtype]).to(H.DEV), v.to(DT[dtype]).to(H.DEV),
+                    cu_t.to(H.DEV), list(lengths))
+
+
+CASES = [
+    # lengths, heads, kv_heads, dim, dtype, ns, layout
+    ([10000], 8, 1, 128, "f32", 7, "packed"),
+    ([10000], 8, 1, 128, "f32", 1000, "packed"),
+    ([1, 2, 3, 17, 64, 65, 300], 28, 4, 128, "f16", 1, "packed"),
+    ([8, 9, 31, 257, 1000, 4097], 28, 4, 128, "f16", 8, "packed"),
+    ([256, 300, 511], 16, 2, 64, "bf16", 16, "bhsd"),
+    ([4096] * 2, 4, 4, 16, "f16", 16, "bhsd"),
+    ([129, 4, 77], 32, 8, 32, "bf16", 4, "packed"),
+    ([5, 33, 1], 6, 2, 16, "f32", 1, "bhsd"),
+    ([100, 37, 64], 32, 2, 128, "f16", 37, "packed"),   # group 16: two row chunks
+    ([3, 10, 5], 8, 1, 64, "f16", 7, "packed"),         # ns > some lengths: empty splits
+    ([0, 12, 40], 8, 2, 128, "bf16", 4, "packed"),      # an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[4]}-d{c[3]}-g{c[1]//c[2]}-ns{c[5]}-{c[6]}")
+def test_split_bounds_and_varlen_indexing_are_exact(case):
+    lengths, heads, kv_heads, dim, dtype, ns, layout = case
+    inp = structured_inputs(lengths, heads, kv_heads, dim, dtype, ns, layout)
+    G = heads // kv_heads
+    ws, opart, lse2 = H.gpu_split(inp, ns, scale=0.37)
+    for b, L in enumerate(lengths):
+        for h in range(heads):
+            j = h // G
+            for s, (a, e) in enumerate(_bounds(L, ns)):
+                n = e - a
+                o = opart[b, h, s]
+                if n == 0:
+                    assert lse2[b, s, h] == -np.inf and not o.any(), (b, h, s)
+                    continue
+                assert round(2.0 ** float(lse2[b, s, h])) == n, (b, h, s, lse2[b, s, h], n)
+                assert round(float(o[0]) * n) == 1 and round(float(o[1]) * n) == 1, (b, h, s)
+                # sequence and KV-head indices come back as exact integers
+                assert round(float(o[2])) == b and round(float(o[3])) == j, (b, h, s, o[2], o[3])
+                assert abs(float(o[2]) - b) <= 1e-6 * max(1, b) and abs(float(o[3]) - j) <= 1e-6 * max(1, j)
+                assert round(float(o[4]) * n) == sum(t % 16 for t in range(a, e)), (b, h, s)
+    out = H.host(H.gpu_attention(inp, ns, scale=0.37))
+    for b, L in enumerate(lengths):
+        for h in range(heads):
+            if L == 0:
+                assert not out[b, h].any()
+                continue
+            assert round(float(out[b, h, 2])) == b and round(float(out[b, h, 3])) == h // G
+            n_nonempty = sum(1 for a, e in _bounds(L, ns) if e > a)
+            assert abs(float(out[b, h, 0]) - n_nonempty / L) <= 1e-2 * max(1.0, n_nonempty / L)
+
+
+# ------------------------------------------------------------ edge cases --
+def _rand_inputs(lengths, heads, kv_heads, dim, dtype, layout="packed", seed=0, pad=0):
+    w = W.Workload("edge", len(lengths), heads, kv_heads, dim, dtype, kv_len=None, layout=layout)
+    return W.make_inputs(w, H.DEV, seed=seed, lengths=lengths, pad_rows=pad)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_key_returns_its_value_exactly(dtype):
+    inp = _rand_inputs([1, 1, 1], 8, 2, 128, dtype)
+    out = H.gpu_attention(inp, 1)
+    G = 4
+    for b in range(3):
+        for h in range(8):
+            assert torch.equal(out[b, h], inp.v[b, h // G]), (b, h)
+
+
+def test_empty_sequence_gives_zero_rows():
+    inp = _rand_inputs([0, 50, 0], 8, 2, 64, "f16", pad=4)
+    for ns in (1, 3):
+        out = H.host(H.gpu_attention(inp, ns))
+        assert not out[0].any() and not out[2].any()
+        ref = oracle.attention_rows(H.host(inp.q[1, 0:4]), H.host(inp.k[0:50, 0]),
+                                    H.host(inp.v[0:50, 0]), 1.0 / math.sqrt(64))
+        assert H.max_err(out[1, 0:4], ref) <= H.TOL["f16"]
+
+
+@pytest.mark.parametrize("layout", ["packed", "bhsd"])
+def test_nan_outside_sequences_is_never_read(layout):
+    inp = _rand_inputs([1, 77, 200, 5], 16, 2, 128, "f16", layout=layout, pad=64)
+    for ns in (1, 5):
+        out = H.host(H.gpu_attention(inp, ns))
+        assert np.isfinite(out).all()
+        ref = H.oracle_full(inp, None)
+        assert H.max_err(out, ref) <= H.TOL["f16"]
+
+
+@pytest.mark.parametrize("group,kv_heads", [(16, 2), (64, 1), (9, 3), (12, 1)])
+def test_groups_larger_than_one_pass(group, kv_heads):
+    inp = _rand_inputs([300, 1025], group * kv_heads, kv_heads, 64, "bf16")
+    for ns in (1, 4):
+        out = H.host(H.gpu_attention(inp, ns))
+        assert H.max_err(out, H.oracle_full(inp, ns)) <= H.TOL["bf16"]
+
+
+@pytest.mark.parametrize("scale", [-0.3, 2.0, 1e-3])
+def test_non_default_scales(scale):
+    inp = _rand_inputs([700, 64, 1], 8, 1, 128, "f32")
+    out = H.host(H.gpu_attention(inp, 1, scale=scale))
+    assert H.max_err(out, H.oracle_full(inp, None, scale=scale)) <= H.TOL["f32"]
+    inp2 = _rand_inputs([700, 64, 3], 8, 1, 128, "f32")
+    out2 = H.host(H.gpu_attention(inp2, 3, scale=scale))
+    assert H.max_err(out2, H.oracle_full(inp2, 3, scale=scale)) <= H.TOL["f32"]
+
+
+def test_repeat_calls_are_bitwise_identical():
+    inp = _rand_inputs([5000, 3000], 28, 4, 128, "f16")
+    a = H.gpu_attention(inp, 8).clone()
+    b = H.gpu_attention(inp, 8).clone()
+    assert torch.equal(a, b)
+    ws1, o1, l1 = H.gpu_split(inp, 8)
+    ws2, o2, l2 = H.gpu_split(inp, 8)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_runs_on_a_side_stream():
+    inp = _rand_inputs([3000, 17], 16, 2, 128, "bf16")
+    ref = H.gpu_attention(inp, 4).clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = H.fd().fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 4, layout="packed",
+                                         stream=s)
+    s.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_split_then_combine_equals_the_whole_call():
+    inp = _rand_inputs([4000, 900], 32, 8, 128, "bf16")
+    fd = H.fd()
+    whole = H.gpu_attention(inp, 6)
+    ws = fd.fd_decode_split(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 6)
+    out = torch.empty_like(inp.q)
+    fd.fd_decode_combine(ws, 2, 32, 128, 6, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, whole)
+
+
+def test_bad_arguments_raise_without_launching():
+    inp = _rand_inputs([10], 8, 2, 128, "f16")
+    fd = H.fd()
+    with pytest.raises(fd.FdError):
+        fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 0)
+    with pytest.raises(fd.FdError):
+        fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 2, scale=float("nan"))
+
+
+# ---------------------------------------------------------- generic grid --
+GRID_LENS = [1, 37, 64, 65, 300, 1029]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dim", [16, 32, 64, 128])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_grid_dims_dtypes_groups(dtype, dim, group):
+    """Ragged lengths spanning one to many tiles, two KV heads, ns=1 and a
+    split count that cuts tiles mid-way."""
+    inp = _rand_inputs(GRID_LENS, 2 * group, 2, dim, dtype, seed=group * 7 + dim)
+    ref = H.oracle_full(inp, None)
+    for ns in (1, 3):
+        out = H.host(H.gpu_attention(inp, ns))
+        err = H.max_err(out, ref)
+        assert err <= H.TOL[dtype], (dtype, dim, group, ns, err)

@@ -19,9 +19,10 @@ the workloads on the pages this project implements:
     Qwen2.5-7B's 28 query heads / 4 KV heads (group 7), head dim 128,
     [total_kv, kv_heads, dim] with int32 cu_seqlens_k.
 
-Recipe: a torch.Generator seeded with ``seed`` (0 by default) on the target
-device draws, in this order, the per-sequence KV lengths when they vary
-(integers uniform in [64, 32768]), then q, K, V as N(0, 1) in float32; the
+Recipe: per-sequence KV lengths, when they vary, are integers uniform in
+[64, 32768] drawn by a CPU torch.Generator seeded with ``seed`` (0 by
+default); then a torch.Generator with the same seed on the target device
+draws q, K, V, in this order, as N(0, 1) in float32; the
 values are then cast to the workload dtype, so every consumer sees identical
 rounded values. Layout "packed" is [total_kv, kv_heads, dim]; layout "bhsd"
 is [batch, kv_heads, max_len, dim]. Optional padding rows past the data are
@@ -169,10 +170,13 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0, pad_rows: int = 0,
     drawn lengths (for edge-case tests).
     """
     device = torch.device(device)
+    if lengths is None:
+        # lengths come from a CPU generator so they do not depend on the device
+        lgen = torch.Generator(device="cpu")
+        lgen.manual_seed(seed)
+        lengths = draw_lengths(w, lgen)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    if lengths is None:
-        lengths = draw_lengths(w, gen)
     lengths = [int(x) for x in lengths]
     if len(lengths) != w.batch:
         raise ValueError("one length per sequence")
