@@ -10,8 +10,9 @@ KV: every step streams its KV from HBM.
 
 Prints ONE JSON line: metric/value (achieved GB/s on the KV bytes of one
 step), ms_per_step, the roofline of the dominant kernel (the split kernel,
-timed by HIP events on the stream it runs on) and the CPU oracle's rate on
-the same workload.
+timed by HIP events on the stream it runs on, over a run of split-only
+launches right after the timed steps) and the CPU oracle's rate on the same
+workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
 """
@@ -138,40 +139,39 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     ws = torch.empty(max(1, fd.fd_workspace_bytes(B, Hq, D, ns)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def split_only(i):
         k, v = ks[i % copies], vs[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         if ns == 1:
             fd.fd_decode_attention(inp.q, k, v, inp.cu_seqlens_k, 1, out=out, layout=w.layout,
                                    stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
         else:
             fd.fd_decode_split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
                                stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
+
+    def step(i):
+        split_only(i)
+        if ns > 1:
             fd.fd_decode_combine(ws, B, Hq, D, ns, out, stream=stream)
+
+    def timed(fn, n, offset):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(n):
+            fn(offset + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, time.perf_counter() - t0
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(steps):
-        step(warmup + i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / steps
-    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    split_avg = sum(split_ms) / len(split_ms)
+    # the timed steps: whole calls, back to back on one stream
+    ms_per_step, wall = timed(step, steps, warmup)
+    # the dominant kernel alone, same inputs and launch configuration
+    split_avg, _ = timed(split_only, steps, warmup + steps)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (split_avg * 1e-3) / 1e9
     res = {
@@ -196,14 +196,25 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic_for(w.name), "kernel": "fd::split_kernel",
                      "kernel_us": round(split_avg * 1e3, 3),
-                     "kernel_us_p10_p90": [round(split_ms[len(split_ms) // 10] * 1e3, 3),
-                                           round(split_ms[(9 * len(split_ms)) // 10] * 1e3, 3)],
                      "algorithmic_bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }
     if cpu_s > 0:
         res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s)
     return res
+
+
+def copy_calibration(mib: int):
+    """Ten device-to-device copies of a mib-MiB buffer: a kernel that reads
+    and writes exactly mib MiB per launch, to scale the HBM byte counters."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": mib << 20, "launches": 10}), flush=True)
 
 
 def main():
@@ -214,7 +225,13 @@ def main():
     ap.add_argument("--workload", default="mha_b4_h32_l4096_d128_f16")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer 10 times (reference for the "
+                         "FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this implementation runs on a single MI355X)", file=sys.stderr)

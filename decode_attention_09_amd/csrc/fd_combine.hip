@@ -7,10 +7,7 @@
 // the combine segment of gqa_decode_splitkv in "decode_attention_splitkv.py"
 // (TileLang tutorial, ch. 18), with the weight of split s for a head applied
 // to that head's row, and the merge of "04_flash_decoding.py" (CS349E
-// lecture 11), demo 1. One wave per (sequence, head): lanes first reduce the
-// LSEs (max, then sum of 2^(lse_s - M)), then stream the fp32 partial rows
-// with coalesced loads, D/64 dims per lane when D >= 64, otherwise several
-// splits side by side; the output is rounded to the input dtype.
+// lecture 11), demo 1. The output is rounded to the input dtype.
 #include "fd_split.h"
 
 namespace fd {
@@ -27,22 +24,41 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int kCombineWaves = 4;
+
+// One workgroup of four waves per (sequence, head). Every thread first helps
+// reduce the split LSEs (max, then sum of 2^(lse_s - max)) through LDS; then
+// each wave streams a strided subset of the partial rows (SPW rows side by
+// side, D/64 dims per lane when D >= 64) and the waves' sums meet in LDS.
 template <int DT, int D>
-__global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineArgs a) {
+  constexpr int NT = kWave * kCombineWaves;
   constexpr int DPL = D >= kWave ? D / kWave : 1;  // dims per lane
   constexpr int LPS = D / DPL;                     // lanes per partial row
-  constexpr int SPW = kWave / LPS;                 // splits read side by side
-  const int lane = threadIdx.x;
+  constexpr int SPW = kWave / LPS;                 // rows a wave reads side by side
+  constexpr int RPG = SPW * kCombineWaves;         // rows the group reads side by side
+  __shared__ float red[kCombineWaves];
+  __shared__ float part[kCombineWaves][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int bh = blockIdx.x;
   const int b = bh / a.heads;
   const int h = bh % a.heads;
   const int ns = a.num_splits;
-  const float* lse = a.lse + (int64_t)b * ns * a.heads + h;  // stride heads
+  const float* lse = a.lse + (int64_t)b * ns * a.heads + h;  // split stride = heads
   const float* op = a.opart + (int64_t)bh * ns * D;
 
   float mx = kNegInf;
-  for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, lse[(int64_t)s * a.heads]);
+  for (int s = tid; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * a.heads]);
   mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineWaves; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
 
   const int sg = lane / LPS;
   const int dl = lane % LPS;
@@ -50,31 +66,36 @@ __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
 
-  if (mx != kNegInf) {
+  if (mx != kNegInf) {  // uniform: every split empty -> zero row
     float tot = 0.0f;
-    for (int s = lane; s < ns; s += kWave) tot += fast_exp2(lse[(int64_t)s * a.heads] - mx);
+    for (int s = tid; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * a.heads] - mx);
     tot = wave_sum(tot);
+    if (lane == 0) red[wave] = tot;
+    __syncthreads();
+    tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) tot += red[w];
     const float lse_all = mx + fast_log2(tot);
-    int s = sg;
-    // four splits in flight per lane group
-    for (; s + 3 * SPW < ns; s += 4 * SPW) {
-      float w[4];
+    int s = wave * SPW + sg;
+    for (; s + 3 * RPG < ns; s += 4 * RPG) {
+      float wt[4];
       float v[4][DPL];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        w[u] = fast_exp2(lse[(int64_t)(s + u * SPW) * a.heads] - lse_all);
+        wt[u] = fast_exp2(lse[(int64_t)(s + u * RPG) * a.heads] - lse_all);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) v[u][e] = op[(int64_t)(s + u * SPW) * D + dl * DPL + e];
+        for (int e = 0; e < DPL; ++e) v[u][e] = op[(int64_t)(s + u * RPG) * D + dl * DPL + e];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(w[u], v[u][e], acc[e]);
+        for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(wt[u], v[u][e], acc[e]);
     }
-    for (; s < ns; s += SPW) {
-      const float w = fast_exp2(lse[(int64_t)s * a.heads] - lse_all);
+    for (; s < ns; s += RPG) {
+      const float wt = fast_exp2(lse[(int64_t)s * a.heads] - lse_all);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(w, op[(int64_t)s * D + dl * DPL + e], acc[e]);
+      for (int e = 0; e < DPL; ++e)
+        acc[e] = __builtin_fmaf(wt, op[(int64_t)s * D + dl * DPL + e], acc[e]);
     }
   }
 #pragma unroll
@@ -83,14 +104,21 @@ __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
     for (int e = 0; e < DPL; ++e) acc[e] += __shfl_xor(acc[e], mask);
   if (sg == 0) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) store_out<DT>(a.out, (int64_t)bh * D + dl * DPL + e, acc[e]);
+    for (int e = 0; e < DPL; ++e) part[wave][dl * DPL + e] = acc[e];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += NT) {
+    float o = part[0][d];
+#pragma unroll
+    for (int w = 1; w < kCombineWaves; ++w) o += part[w][d];
+    store_out<DT>(a.out, (int64_t)bh * D + d, o);
   }
 }
 
 template <int DT>
 static hipError_t launch_combine_dt(const CombineArgs& a, int dim, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.heads));
-  dim3 block(kWave);
+  dim3 block(kWave * kCombineWaves);
   switch (dim) {
     case 16: hipLaunchKernelGGL((combine_kernel<DT, 16>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((combine_kernel<DT, 32>), grid, block, 0, s, a); break;
