@@ -53,9 +53,11 @@ def workload_by_name(name: str):
                      + ", ".join(w.name for w in W.all_workloads()))
 
 
-def pick_splits(w, lengths):
+def pick_splits(w, lengths, override=0):
     import workloads as W
     import decode_attention_09_amd as fd
+    if override:
+        return override
     if w.num_splits is not None:
         return W.varlen_splits(w, lengths) if w.varlen_range else w.num_splits
     code = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}[w.dtype]
@@ -121,7 +123,8 @@ def cpu_baseline(inp, ns, budget_s: float):
     }
 
 
-def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES):
+def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES,
+        ns_override: int = 0):
     import torch
     import workloads as W
     import decode_attention_09_amd as fd
@@ -129,7 +132,7 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = W.make_inputs(w, dev, seed=0)
-    ns = pick_splits(w, inp.lengths)
+    ns = pick_splits(w, inp.lengths, ns_override)
     kv_bytes = inp.kv_bytes
     copies = max(1, min(16, math.ceil(copies_min_bytes / max(1, kv_bytes))))
     ks = [inp.k] + [inp.k.clone() for _ in range(copies - 1)]
@@ -138,20 +141,17 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     B, Hq, D = w.batch, w.heads, w.dim
     ws = torch.empty(max(1, fd.fd_workspace_bytes(B, Hq, D, ns)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    single_launch = ns == 1
+
+    def step(i):
+        k, v = ks[i % copies], vs[i % copies]
+        fd.fd_decode_attention(inp.q, k, v, inp.cu_seqlens_k, ns, out=out, workspace=ws,
+                               layout=w.layout, stream=stream)
 
     def split_only(i):
         k, v = ks[i % copies], vs[i % copies]
-        if ns == 1:
-            fd.fd_decode_attention(inp.q, k, v, inp.cu_seqlens_k, 1, out=out, layout=w.layout,
-                                   stream=stream)
-        else:
-            fd.fd_decode_split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
-                               stream=stream)
-
-    def step(i):
-        split_only(i)
-        if ns > 1:
-            fd.fd_decode_combine(ws, B, Hq, D, ns, out, stream=stream)
+        fd.fd_decode_split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
+                           stream=stream)
 
     def timed(fn, n, offset):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -170,8 +170,9 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     torch.cuda.synchronize()
     # the timed steps: whole calls, back to back on one stream
     ms_per_step, wall = timed(step, steps, warmup)
-    # the dominant kernel alone, same inputs and launch configuration
-    split_avg, _ = timed(split_only, steps, warmup + steps)
+    # the dominant kernel: with one split the whole step is that one launch;
+    # otherwise the split kernel alone, same inputs and launch configuration
+    split_avg = ms_per_step if single_launch else timed(split_only, steps, warmup + steps)[0]
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (split_avg * 1e-3) / 1e9
     res = {
@@ -194,7 +195,8 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
                    "kv_copies_rotated": copies, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": traffic_for(w.name), "kernel": "fd::split_kernel",
+                     "traffic": traffic_for(w.name),
+                     "kernel": "split kernel",
                      "kernel_us": round(split_avg * 1e3, 3),
                      "algorithmic_bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
@@ -225,6 +227,10 @@ def main():
     ap.add_argument("--workload", default="mha_b4_h32_l4096_d128_f16")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="override the workload's split count (sweeps)")
+    ap.add_argument("--kernel-path", choices=["auto", "valu", "mfma"], default="auto",
+                    help="split kernel variant (default: the library's own choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 10 times (reference for the "
                          "FETCH_SIZE/WRITE_SIZE counters)")
@@ -236,16 +242,22 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this implementation runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    import decode_attention_09_amd as fd
+    fd.fd_set_kernel_path({"auto": fd.FD_PATH_AUTO, "valu": fd.FD_PATH_VALU,
+                           "mfma": fd.FD_PATH_MFMA}[args.kernel_path])
     if args.all:
         import workloads as W
         for w in W.all_workloads():
             r = run(w, args.steps, args.warmup, 0.0)
+            r["kernel_path"] = args.kernel_path
             print(json.dumps(r), flush=True)
             import torch
             torch.cuda.empty_cache()
         return
-    print(json.dumps(run(workload_by_name(args.workload), args.steps, args.warmup,
-                         args.cpu_seconds)), flush=True)
+    r = run(workload_by_name(args.workload), args.steps, args.warmup, args.cpu_seconds,
+            ns_override=args.num_splits)
+    r["kernel_path"] = args.kernel_path
+    print(json.dumps(r), flush=True)
 
 
 if __name__ == "__main__":

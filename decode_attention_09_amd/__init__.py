@@ -15,11 +15,13 @@ import os
 __all__ = [
     "FD_F32", "FD_F16", "FD_BF16", "FD_MAX_SPLITS", "FdError", "library_path", "load_library",
     "fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
-    "fd_decode_combine", "fd_status_string", "fd_last_error", "kv_layout",
+    "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path", "kv_layout",
+    "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "workspace_views",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_MAX_SPLITS = 16384
+FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = 0, 1, 2
 _STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
            3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP"}
 
@@ -50,6 +52,11 @@ def load_library():
     global _LIB
     if _LIB is not None:
         return _LIB
+    # torch ships its own HIP runtime under the same soname as the system one.
+    # Import it first so libfd binds to the runtime that owns the tensors and
+    # streams it is handed (loading libfd first would bring in a second HIP
+    # runtime, on which the device is not visible).
+    import torch  # noqa: F401
     path = library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
@@ -73,6 +80,8 @@ def load_library():
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
     lib.fd_last_error.restype = ctypes.c_char_p
+    lib.fd_set_kernel_path.argtypes = [i32]
+    lib.fd_set_kernel_path.restype = i32
     _LIB = lib
     return lib
 
@@ -88,6 +97,15 @@ def fd_status_string(status: int) -> str:
 
 def fd_last_error() -> str:
     return load_library().fd_last_error().decode()
+
+
+def fd_set_kernel_path(path: int) -> int:
+    """Select the split kernel (FD_PATH_AUTO / _VALU / _MFMA); returns the
+    previous setting."""
+    prev = load_library().fd_set_kernel_path(int(path))
+    if prev < 0:
+        raise ValueError(f"unknown kernel path {path}")
+    return prev
 
 
 # ----------------------------------------------------------- marshalling --
@@ -220,3 +238,4 @@ def workspace_views(workspace, batch: int, heads: int, dim: int, num_splits: int
     lse = flat[off:off + batch * num_splits * heads * 4].view(torch.float32).view(
         batch, num_splits, heads)
     return opart, lse
+

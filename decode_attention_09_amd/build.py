@@ -37,29 +37,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfd)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _flags():
+    # FD_HIPCC_FLAGS: extra hipcc flags (e.g. -DFD_PREFETCH_TILES=2)
+    return FLAGS + os.environ.get("FD_HIPCC_FLAGS", "").split()
+
+
+def _compile(src: str, obj_dir: str = OBJ) -> str:
+    obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, lib_path: str = LIB, obj_dir: str = OBJ) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, obj_dir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

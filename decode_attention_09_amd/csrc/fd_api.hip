@@ -11,6 +11,7 @@
 // be empty.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -22,6 +23,15 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+std::atomic<int> g_path{FD_PATH_AUTO};
+
+// The library's own choice of split kernel: matrix-core QK^T wherever that
+// kernel exists (16-bit inputs, head dim 128). Measured on MI355X it is
+// faster at groups of 4-8 (2.4x fewer VALU instructions) and no slower at 1.
+bool auto_mfma(int dtype, int dim, int group) {
+  (void)group;
+  return dtype != FD_F32 && dim == 128;
+}
 
 int hip_fail(hipError_t e, const char* where) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
@@ -31,12 +41,13 @@ int hip_fail(hipError_t e, const char* where) {
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int64_t kMaxWorkgroups = int64_t(1) << 24;
-// Resident split workgroups per compute unit assumed by the planner (the
-// split kernel's 4-wave workgroups at its register footprint).
-constexpr int kPlanGroupsPerCu = 2;
 // Fewest keys per split the planner will create (flash_decode_splitk.py's
 // default of one split per 256 keys).
 constexpr int kPlanMinKeysPerSplit = 256;
+// Fixed cost of one split workgroup (launch, first-tile latency, epilogue),
+// as the equivalent bytes a compute unit streams in that time (measured on
+// MI355X: about 1 us at ~25-30 GB/s per CU).
+constexpr double kPlanWorkgroupBytes = 32.0 * 1024.0;
 
 int elem_bytes(int dtype) { return dtype == FD_F32 ? 4 : 2; }
 
@@ -115,16 +126,19 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.direct = direct;
   a.scale_log2 = (float)((double)scale * kLog2e);
   dim3 grid((unsigned)sz.workgroups);
+  const int path = g_path.load(std::memory_order_relaxed);
+  const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;
   switch (dtype) {
-    case FD_F32: e = fd::launch_split_f32(a, dim, sz.rows, grid, stream); break;
-    case FD_F16: e = fd::launch_split_f16(a, dim, sz.rows, grid, stream); break;
-    default: e = fd::launch_split_bf16(a, dim, sz.rows, grid, stream); break;
+    case FD_F32: e = fd::launch_split_f32(a, dim, sz.rows, mfma, grid, stream); break;
+    case FD_F16: e = fd::launch_split_f16(a, dim, sz.rows, mfma, grid, stream); break;
+    default: e = fd::launch_split_bf16(a, dim, sz.rows, mfma, grid, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
   return FD_OK;
 }
 
+// Workspace: [Opart][pad to 256 B][LSE].
 size_t opart_bytes(int batch, int heads, int dim, int num_splits) {
   return (size_t)batch * heads * num_splits * dim * sizeof(float);
 }
@@ -154,10 +168,12 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
   int st = check_common(batch, heads, kv_heads, dim, 1, dtype, &sz);
   if (st != FD_OK) return st;
   int64_t min_len = INT64_MAX, max_len = 0;
+  double total_keys = 0.0;
   for (int b = 0; b < batch; ++b) {
     const int64_t x = seqlens_host[b];
     if (x < min_len) min_len = x;
     if (x > max_len) max_len = x;
+    total_keys += (double)x;
   }
   if (min_len < 1) return FD_ERR_EMPTY_SPLIT;
   if (num_cus < 0) return FD_ERR_INVALID_ARG;
@@ -169,7 +185,7 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   }
   if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
-  // candidate range: every split non-empty, the longest sequence keeps
+  // candidates: every split non-empty, the longest sequence keeps
   // >= kPlanMinKeysPerSplit keys per split, workgroup count bounded
   int64_t cap = (max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
   if (cap > min_len) cap = min_len;
@@ -177,24 +193,32 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
   const int64_t units = (int64_t)batch * kv_heads * sz.row_chunks;
   while (cap > 1 && units * cap > kMaxWorkgroups) --cap;
   if (cap < 1) cap = 1;
-  const int64_t slots = (int64_t)num_cus * kPlanGroupsPerCu;
-  // fill(ns): share of workgroup slots busy, averaged over the passes
-  // needed (wave quantisation); pick the smallest ns within 90% of the best.
+  // Estimated time, in bytes one compute unit streams, of a launch with ns
+  // splits on P = num_cus units: each unit runs `passes` rounds of
+  // workgroups (the workgroup count quantised to the CU count, the wave
+  // quantisation of 04_flash_decoding.py demo 4), each round paying the
+  // fixed workgroup cost. Equal lengths: every workgroup streams the same
+  // bytes, so a unit streams passes x that. Unequal lengths: workgroups are
+  // handed out as units free up, which finishes within the average load
+  // plus the largest workgroup (list-scheduling bound).
+  const double P = (double)num_cus;
+  const double key_bytes = 2.0 * dim * (dtype == FD_F32 ? 4 : 2);  // one K + one V row
+  const double all_bytes = total_keys * (double)kv_heads * sz.row_chunks * key_bytes;
+  const bool uniform = min_len == max_len;
   double best = 0.0;
-  for (int64_t ns = 1; ns <= cap; ++ns) {
-    const int64_t wgs = units * ns;
-    const int64_t passes = (wgs + slots - 1) / slots;
-    const double fill = (double)wgs / (double)(passes * slots);
-    if (fill > best) best = fill;
-  }
   int choice = 1;
   for (int64_t ns = 1; ns <= cap; ++ns) {
-    const int64_t wgs = units * ns;
-    const int64_t passes = (wgs + slots - 1) / slots;
-    const double fill = (double)wgs / (double)(passes * slots);
-    if (fill >= 0.9 * best) {
+    const double wgs = (double)(units * ns);
+    const double passes = std::ceil(wgs / P);
+    const double wg_max = std::ceil((double)max_len / (double)ns) * key_bytes;
+    double t = passes * kPlanWorkgroupBytes;
+    if (uniform)
+      t += passes * wg_max;
+    else
+      t += all_bytes / P + wg_max;
+    if (ns == 1 || t < best) {
+      best = t;
       choice = (int)ns;
-      break;
     }
   }
   *num_splits_out = choice;
@@ -280,5 +304,10 @@ const char* fd_status_string(int status) {
 }
 
 const char* fd_last_error(void) { return g_last_error; }
+
+int fd_set_kernel_path(int path) {
+  if (path != FD_PATH_AUTO && path != FD_PATH_VALU && path != FD_PATH_MFMA) return -1;
+  return g_path.exchange(path);
+}
 
 }  // extern "C"

@@ -1,17 +1,20 @@
-// Combine kernel of flash decoding for gfx950: merges the per-split
-// normalised partial outputs with their base-2 log-sum-exps,
-//
-//   M = max_s lse_s,  lse = M + log2 sum_s 2^(lse_s - M),
-//   o = sum_s 2^(lse_s - lse) * o_s,
-//
-// the combine segment of gqa_decode_splitkv in "decode_attention_splitkv.py"
-// (TileLang tutorial, ch. 18), with the weight of split s for a head applied
-// to that head's row, and the merge of "04_flash_decoding.py" (CS349E
-// lecture 11), demo 1. The output is rounded to the input dtype.
+// Combine kernel of flash decoding for gfx950, the second launch: merges
+// the per-split normalised partial outputs with their base-2 log-sum-exps
+// into the output.
 #include "fd_split.h"
 
 namespace fd {
 
+// The LSE merge of one (sequence, head) by a workgroup of NWAVES waves:
+//   M = max_s lse_s, lse = M + log2 sum_s 2^(lse_s - M),
+//   o = sum_s 2^(lse_s - lse) * o_s,   rounded to the dtype,
+// the combine segment of gqa_decode_splitkv in "decode_attention_splitkv.py"
+// (TileLang tutorial, ch. 18), with the weight of split s for a head applied
+// to that head's row, and the merge of "04_flash_decoding.py" (CS349E
+// lecture 11), demo 1. Every thread first helps reduce the LSEs through
+// LDS; then each wave streams a strided subset of the partial rows (SPW rows
+// side by side, D/64 dims per lane when D >= 64) and the waves' sums meet in
+// LDS. All threads of the workgroup must call it (it synchronises).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int mask = 1; mask < kWave; mask <<= 1) x = fmaxf(x, __shfl_xor(x, mask));
@@ -24,40 +27,32 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-constexpr int kCombineWaves = 4;
-
-// One workgroup of four waves per (sequence, head). Every thread first helps
-// reduce the split LSEs (max, then sum of 2^(lse_s - max)) through LDS; then
-// each wave streams a strided subset of the partial rows (SPW rows side by
-// side, D/64 dims per lane when D >= 64) and the waves' sums meet in LDS.
-template <int DT, int D>
-__global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineArgs a) {
-  constexpr int NT = kWave * kCombineWaves;
+template <int DT, int D, int NWAVES>
+__device__ __forceinline__ void combine_head(const float* opart, const float* lse_base, void* out,
+                                             int heads, int ns, int b, int h) {
+  constexpr int NT = kWave * NWAVES;
   constexpr int DPL = D >= kWave ? D / kWave : 1;  // dims per lane
   constexpr int LPS = D / DPL;                     // lanes per partial row
   constexpr int SPW = kWave / LPS;                 // rows a wave reads side by side
-  constexpr int RPG = SPW * kCombineWaves;         // rows the group reads side by side
-  __shared__ float red[kCombineWaves];
-  __shared__ float part[kCombineWaves][D];
+  constexpr int RPG = SPW * NWAVES;                // rows the group reads side by side
+  __shared__ float red[NWAVES];
+  __shared__ float part[NWAVES][D];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int bh = blockIdx.x;
-  const int b = bh / a.heads;
-  const int h = bh % a.heads;
-  const int ns = a.num_splits;
-  const float* lse = a.lse + (int64_t)b * ns * a.heads + h;  // split stride = heads
-  const float* op = a.opart + (int64_t)bh * ns * D;
+  const int64_t bh = (int64_t)b * heads + h;
+  const float* lse = lse_base + (int64_t)b * ns * heads + h;  // split stride = heads
+  const float* op = opart + bh * ns * D;
 
   float mx = kNegInf;
-  for (int s = tid; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * a.heads]);
+  for (int s = tid; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * heads]);
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   mx = red[0];
 #pragma unroll
-  for (int w = 1; w < kCombineWaves; ++w) mx = fmaxf(mx, red[w]);
+  for (int w = 1; w < NWAVES; ++w) mx = fmaxf(mx, red[w]);
   __syncthreads();
 
   const int sg = lane / LPS;
@@ -68,13 +63,13 @@ __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineAr
 
   if (mx != kNegInf) {  // uniform: every split empty -> zero row
     float tot = 0.0f;
-    for (int s = tid; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * a.heads] - mx);
+    for (int s = tid; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * heads] - mx);
     tot = wave_sum(tot);
     if (lane == 0) red[wave] = tot;
     __syncthreads();
     tot = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kCombineWaves; ++w) tot += red[w];
+    for (int w = 0; w < NWAVES; ++w) tot += red[w];
     const float lse_all = mx + fast_log2(tot);
     int s = wave * SPW + sg;
     for (; s + 3 * RPG < ns; s += 4 * RPG) {
@@ -82,9 +77,10 @@ __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineAr
       float v[4][DPL];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wt[u] = fast_exp2(lse[(int64_t)(s + u * RPG) * a.heads] - lse_all);
+        wt[u] = fast_exp2(lse[(int64_t)(s + u * RPG) * heads] - lse_all);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) v[u][e] = op[(int64_t)(s + u * RPG) * D + dl * DPL + e];
+        for (int e = 0; e < DPL; ++e)
+          v[u][e] = op[(int64_t)(s + u * RPG) * D + dl * DPL + e];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -92,7 +88,7 @@ __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineAr
         for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(wt[u], v[u][e], acc[e]);
     }
     for (; s < ns; s += RPG) {
-      const float wt = fast_exp2(lse[(int64_t)s * a.heads] - lse_all);
+      const float wt = fast_exp2(lse[(int64_t)s * heads] - lse_all);
 #pragma unroll
       for (int e = 0; e < DPL; ++e)
         acc[e] = __builtin_fmaf(wt, op[(int64_t)s * D + dl * DPL + e], acc[e]);
@@ -110,9 +106,19 @@ __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineAr
   for (int d = tid; d < D; d += NT) {
     float o = part[0][d];
 #pragma unroll
-    for (int w = 1; w < kCombineWaves; ++w) o += part[w][d];
-    store_out<DT>(a.out, (int64_t)bh * D + d, o);
+    for (int w = 1; w < NWAVES; ++w) o += part[w][d];
+    store_out<DT>(out, bh * D + d, o);
   }
+}
+
+constexpr int kCombineWaves = 4;
+
+// One workgroup of four waves per (sequence, head).
+template <int DT, int D>
+__global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineArgs a) {
+  const int bh = blockIdx.x;
+  combine_head<DT, D, kCombineWaves>(a.opart, a.lse, a.out, a.heads, a.num_splits,
+                                     bh / a.heads, bh % a.heads);
 }
 
 template <int DT>

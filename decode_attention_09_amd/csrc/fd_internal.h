@@ -11,6 +11,11 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;  // waves per split workgroup
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
 constexpr int kLoadsPerTile = 4;   // 16-byte K (and V) loads per lane per tile
+#ifndef FD_PREFETCH_TILES
+#define FD_PREFETCH_TILES 1
+#endif
+// Tiles whose loads are in flight while a wave computes the current one.
+constexpr int kPrefetchTiles = FD_PREFETCH_TILES;
 
 // Arguments of the split kernel (passed by value).
 struct SplitArgs {
@@ -36,9 +41,14 @@ struct CombineArgs {
 
 // Launchers (defined in fd_split_<dtype>.hip and fd_combine.hip). They
 // return the hipError_t of the launch.
-hipError_t launch_split_f32(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
-hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
-hipError_t launch_split_bf16(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s);
+// `mfma` selects the matrix-core QK^T kernel where one exists (16-bit
+// inputs, head dim 128); otherwise the VALU kernel runs.
+hipError_t launch_split_f32(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
+                            hipStream_t s);
+hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
+                            hipStream_t s);
+hipError_t launch_split_bf16(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
+                             hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s);
 
 }  // namespace fd

@@ -31,9 +31,11 @@
 //    masked out of the softmax.
 //  * Four waves per workgroup take interleaved tiles of the segment and are
 //    merged through LDS at the end (the same LSE merge as the combine).
-//  * Double-buffered register tiles: the next tile's loads are issued
-//    before the current tile is computed.
+//  * Register tile pipeline: the loads of the next kPrefetchTiles tiles are
+//    in flight while the current tile is computed.
 #pragma once
+
+#include <type_traits>
 
 #include "fd_internal.h"
 
@@ -154,7 +156,135 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
     static_cast<__bf16*>(out)[idx] = (__bf16)x;
 }
 
-// --------------------------------------------------------------- kernel --
+// ------------------------------------------------------- work decoding --
+// Where one split workgroup works: workgroup -> (split, KV head, row chunk,
+// sequence), split index fastest; varlen bounds from cu_seqlens_k and the
+// proportional segment [L*s/ns, L*(s+1)/ns) with 64-bit products.
+struct Segment {
+  int b, sid, kvh, h0, nrows;
+  int64_t nkeys;
+  const char* k;   // first K row of the segment
+  const char* v;   // first V row of the segment
+  uint32_t tsb;    // bytes between consecutive keys
+};
+
+template <int EB, int GC>
+__device__ __forceinline__ Segment locate_segment(const SplitArgs& a) {
+  Segment g;
+  int wg = blockIdx.x;
+  const int ns = a.num_splits;
+  g.sid = wg % ns;
+  wg /= ns;
+  const int hcn = a.kv_heads * a.row_chunks;
+  const int hc = wg % hcn;
+  g.b = wg / hcn;
+  g.kvh = hc / a.row_chunks;
+  const int chunk = hc % a.row_chunks;
+  g.h0 = g.kvh * a.group + chunk * kMaxRowsPerPass;
+  g.nrows = min(GC, a.group - chunk * kMaxRowsPerPass);
+  const int cu0 = a.cu[g.b];
+  const int cu1 = a.cu[g.b + 1];
+  const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
+  const int64_t seg0 = L * g.sid / ns;
+  g.nkeys = L * (g.sid + 1) / ns - seg0;
+  const int64_t row0 =
+      (int64_t)g.b * a.sb + (int64_t)cu0 * a.scu + (int64_t)g.kvh * a.sh + seg0 * a.st;
+  g.k = static_cast<const char*>(a.k) + row0 * EB;
+  g.v = static_cast<const char*>(a.v) + row0 * EB;
+  g.tsb = (uint32_t)(a.st * EB);
+  return g;
+}
+
+// Descriptors for tile j of TK keys of a segment: sized to end at the last
+// valid row, empty for a tile past the segment (its loads return zeros).
+template <int TK, int ROWB>
+__device__ __forceinline__ void tile_rsrc(const Segment& sg, int j, __amdgpu_buffer_rsrc_t& rk,
+                                          __amdgpu_buffer_rsrc_t& rv) {
+  const int64_t k0 = (int64_t)j * TK;
+  const int64_t nv = sg.nkeys - k0;
+  const uint32_t rec = nv > 0 ? (uint32_t)((min(nv, (int64_t)TK) - 1) * sg.tsb + ROWB) : 0u;
+  const int64_t off = nv > 0 ? k0 * sg.tsb : 0;
+  rk = make_rsrc(sg.k + off, rec);
+  rv = make_rsrc(sg.v + off, rec);
+}
+
+// Merge the per-wave states (max, sum, unnormalised acc) left in LDS and
+// write the split epilogue: o_s = acc / l and lse2_s = log2(l) + m, or the
+// final output in dtype when the call has a single split.
+template <int DT, int D, int GC, int NW>
+__device__ __forceinline__ void store_segment(const SplitArgs& a, const Segment& sg,
+                                              const float (&sm_m)[NW][GC],
+                                              const float (&sm_l)[NW][GC],
+                                              const float (&sm_acc)[NW][GC][D]) {
+  const int ns = a.num_splits;
+  for (int idx = threadIdx.x; idx < sg.nrows * D; idx += NW * kWave) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float M = sm_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = sm_m[w][g] == kNegInf ? 0.0f : fast_exp2(sm_m[w][g] - M);
+      lsum += f * sm_l[w][g];
+      o += f * sm_acc[w][g][d];
+    }
+    const bool any = lsum > 0.0f;
+    o = any ? o / lsum : 0.0f;
+    const int h = sg.h0 + g;
+    if (a.direct) {
+      store_out<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, o);
+    } else {
+      a.opart[(((int64_t)sg.b * a.heads + h) * ns + sg.sid) * D + d] = o;
+      if (d == 0)
+        a.lse[((int64_t)sg.b * ns + sg.sid) * a.heads + h] = any ? fast_log2(lsum) + M : kNegInf;
+    }
+  }
+}
+
+// ------------------------------------------------------------ pipeline --
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+// A wave's walk over the tiles first, first+NW, ... (< nt) of its segment
+// with PF tiles' loads in flight while it computes one: PF+1 register
+// buffers used round-robin, the loop unrolled so every buffer index is a
+// constant. Loads of tiles past the segment are harmless (empty
+// descriptors); the walk stops after the last tile. The scheduling barriers
+// keep each prefetch ahead of the compute it overlaps.
+template <int PF, int NW, typename Tile, typename Load, typename Compute>
+__device__ __forceinline__ void tile_pipeline(int first, int nt, Load&& load, Compute&& compute) {
+  if (first >= nt) return;  // uniform: this wave has no tile of the segment
+  Tile buf[PF + 1];
+  static_for<PF>([&](auto ui) {
+    constexpr int u = decltype(ui)::value;
+    load(first + u * NW, buf[u]);
+  });
+  int j = first;
+  while (true) {
+    bool done = false;
+    static_for<PF + 1>([&](auto ui) {
+      constexpr int u = decltype(ui)::value;
+      if (!done) {
+        load(j + PF * NW, buf[(u + PF) % (PF + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j, buf[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        j += NW;
+        done = j >= nt;
+      }
+    });
+    if (done) break;
+  }
+}
+
+// --------------------------------------------------------- VALU kernel --
 template <int DT, int D, int GC>
 __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs a) {
   constexpr int EB = Elem<DT>::bytes;
@@ -174,33 +304,16 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
   const int rg = lane / LPR;  // which row of a load this lane holds
   const int c = lane % LPR;   // which 16-byte chunk of the row
 
-  // workgroup -> (split, KV head, row chunk, sequence); split fastest.
-  int wg = blockIdx.x;
-  const int ns = a.num_splits;
-  const int sid = wg % ns;
-  wg /= ns;
-  const int hcn = a.kv_heads * a.row_chunks;
-  const int hc = wg % hcn;
-  const int b = wg / hcn;
-  const int kvh = hc / a.row_chunks;
-  const int chunk = hc % a.row_chunks;
-  const int h0 = kvh * a.group + chunk * kMaxRowsPerPass;
-  const int nrows = min(GC, a.group - chunk * kMaxRowsPerPass);
-
-  // varlen bounds and proportional segment (64-bit products)
-  const int cu0 = a.cu[b];
-  const int cu1 = a.cu[b + 1];
-  const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
-  const int64_t seg0 = L * sid / ns;
-  const int64_t nkeys = L * (sid + 1) / ns - seg0;
+  const Segment sg = locate_segment<EB, GC>(a);
+  const int64_t nkeys = sg.nkeys;
 
   // q chunks of the packed rows (rows past the group read as zero)
   u4_t q[GC];
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    if (g < nrows) {
+    if (g < sg.nrows) {
       const char* qp = static_cast<const char*>(a.q) +
-                       (((int64_t)b * a.heads + h0 + g) * D + c * EPL) * EB;
+                       (((int64_t)sg.b * a.heads + sg.h0 + g) * D + c * EPL) * EB;
       q[g] = *reinterpret_cast<const u4_t*>(qp);
     } else {
       q[g] = u4_t{0u, 0u, 0u, 0u};
@@ -212,12 +325,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     }
   }
   const float score_mul = DT == DT_F32 ? 1.0f : a.scale_log2;
-
-  const int64_t row0 = (int64_t)b * a.sb + (int64_t)cu0 * a.scu + (int64_t)kvh * a.sh + seg0 * a.st;
-  const char* kseg = static_cast<const char*>(a.k) + row0 * EB;
-  const char* vseg = static_cast<const char*>(a.v) + row0 * EB;
-  const uint32_t tsb = (uint32_t)(a.st * EB);  // bytes between consecutive keys
-  const uint32_t lane_off = (uint32_t)rg * tsb + (uint32_t)c * 16u;
+  const uint32_t lane_off = (uint32_t)rg * sg.tsb + (uint32_t)c * 16u;
 
   float m[GC], l[GC], acc[GC][EPL];
 #pragma unroll
@@ -230,23 +338,20 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
 
   const int nt = (int)((nkeys + TK - 1) / TK);
 
-  // Loads of tile j; a tile past the segment gets an empty descriptor, so
-  // the loads are unconditional and return zeros.
-  auto load_tile = [&](int j, u4_t (&kt)[NI], u4_t (&vt)[NI]) {
-    const int64_t k0 = (int64_t)j * TK;
-    const int64_t nv = nkeys - k0;
-    const uint32_t rec = nv > 0 ? (uint32_t)((min(nv, (int64_t)TK) - 1) * tsb + D * EB) : 0u;
-    const char* kb = kseg + (nv > 0 ? k0 * tsb : 0);
-    const char* vb = vseg + (nv > 0 ? k0 * tsb : 0);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, rec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, rec);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) kt[i] = buffer_load16(rk, lane_off + (uint32_t)(i * RPI) * tsb);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vt[i] = buffer_load16(rv, lane_off + (uint32_t)(i * RPI) * tsb);
+  struct Tile {
+    u4_t k[NI], v[NI];
   };
-
-  auto compute_tile = [&](int j, const u4_t (&kt)[NI], const u4_t (&vt)[NI]) {
+  auto load_tile = [&](int j, Tile& t) {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    tile_rsrc<TK, D * EB>(sg, j, rk, rv);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) t.k[i] = buffer_load16(rk, lane_off + (uint32_t)(i * RPI) * sg.tsb);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) t.v[i] = buffer_load16(rv, lane_off + (uint32_t)(i * RPI) * sg.tsb);
+  };
+  auto compute_tile = [&](int j, const Tile& t) {
+    const u4_t(&kt)[NI] = t.k;
+    const u4_t(&vt)[NI] = t.v;
     const int64_t k0 = (int64_t)j * TK;
     float s[NI][GC];
     bool valid[NI];
@@ -311,26 +416,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     }
   };
 
-  {
-    u4_t ka[NI], va[NI], kb[NI], vb[NI];
-    int j = wave;
-    load_tile(j, ka, va);
-    // The scheduling barriers keep each prefetch ahead of the compute it
-    // overlaps (the scheduler would otherwise sink loads past waits).
-    while (j < nt) {
-      load_tile(j + NW, kb, vb);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(j, ka, va);
-      __builtin_amdgcn_sched_barrier(0);
-      j += NW;
-      if (j >= nt) break;
-      load_tile(j + NW, ka, va);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(j, kb, vb);
-      __builtin_amdgcn_sched_barrier(0);
-      j += NW;
-    }
-  }
+  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, load_tile, compute_tile);
 
   // ---- merge the lane groups of this wave (each has its own max) ----
 #pragma unroll
@@ -367,37 +453,222 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     }
   }
   __syncthreads();
-
-  for (int idx = tid; idx < nrows * D; idx += NW * kWave) {
-    const int g = idx / D;
-    const int d = idx % D;
-    float M = sm_m[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = sm_m[w][g] == kNegInf ? 0.0f : fast_exp2(sm_m[w][g] - M);
-      lsum += f * sm_l[w][g];
-      o += f * sm_acc[w][g][d];
-    }
-    const bool any = lsum > 0.0f;
-    o = any ? o / lsum : 0.0f;
-    const int h = h0 + g;
-    if (a.direct) {
-      store_out<DT>(a.out, ((int64_t)b * a.heads + h) * D + d, o);
-    } else {
-      a.opart[(((int64_t)b * a.heads + h) * ns + sid) * D + d] = o;
-      if (d == 0)
-        a.lse[((int64_t)b * ns + sid) * a.heads + h] = any ? fast_log2(lsum) + M : kNegInf;
-    }
-  }
+  store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
 }
 
-// Host-side dispatch over (D, rows) for one dtype.
+// --------------------------------------------------------- MFMA kernel --
+// Same contract as split_kernel, for fp16/bf16 at head dim 128, with QK^T on
+// the matrix cores. Per wave tile of 16 keys:
+//  * S^T[16 keys x 16 cols] = K[16 x 128] . Q^T[128 x 16] as four
+//    v_mfma_f32_16x16x32_{f16,bf16}: lane (R = lane/16, c = lane%16) feeds
+//    row c of K (dims 32m + 8R .. +8 for step m, one 16-byte load each) and
+//    column c of Q^T (query row c of the group, zero past the group), and
+//    receives S for query row g = c and keys 4R + r, r = 0..3.
+//  * Online softmax runs per lane on those four scores (per (R, g) running
+//    max and sum, lazily rescaled as in split_kernel): no cross-lane work.
+//  * PV stays on the VALU with v_dot2: lane (R, c) holds dims 8c..8c+7 of
+//    keys 4R + i (V loads of whole 256-byte rows) and takes the packed
+//    probability pair of query row g from lane (R, g) of its own 16-lane row
+//    with DPP row_newbcast.
+// The workgroup epilogue is shared with split_kernel.
+template <int LANE>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + LANE, 0xF, 0xF, false);
+}
+
+template <int LANE>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, row_bcast<LANE>(__builtin_bit_cast(uint32_t, x)));
+}
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, k),
+                                                  __builtin_bit_cast(h8_t, q), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, k),
+                                                   __builtin_bit_cast(b8_t, q), acc, 0, 0, 0);
+}
+
+template <int DT, int GC>
+__global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(SplitArgs a) {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "matrix-core path takes 16-bit inputs");
+  static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
+  constexpr int D = 128;
+  constexpr int EB = 2;
+  constexpr int TK = 16;           // keys per wave tile
+  constexpr int KS = D / 32;       // MFMA k-steps per tile
+  constexpr int NW = kWavesPerGroup;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int R = lane >> 4;   // key group of this lane
+  const int c = lane & 15;   // K row / query row / V chunk of this lane
+
+  const Segment sg = locate_segment<EB, GC>(a);
+  const int64_t nkeys = sg.nkeys;
+
+  // Q^T as the MFMA B operand: column c = query row h0 + c
+  u4_t qb[KS];
+#pragma unroll
+  for (int m = 0; m < KS; ++m) {
+    if (c < sg.nrows) {
+      const char* qp = static_cast<const char*>(a.q) +
+                       (((int64_t)sg.b * a.heads + sg.h0 + c) * D + 32 * m + 8 * R) * EB;
+      qb[m] = *reinterpret_cast<const u4_t*>(qp);
+    } else {
+      qb[m] = u4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  const uint32_t k_off = (uint32_t)c * sg.tsb + (uint32_t)R * 16u;       // + 64*m
+  const uint32_t v_off = (uint32_t)(4 * R) * sg.tsb + (uint32_t)c * 16u;  // + i*tsb
+
+  float m_run = kNegInf, l_run = 0.0f;  // for (key group R, query row c)
+  float acc[GC][8];
+#pragma unroll
+  for (int g = 0; g < GC; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+
+  const int nt = (int)((nkeys + TK - 1) / TK);
+
+  struct Tile {
+    u4_t k[KS], v[4];
+  };
+  auto load_tile = [&](int j, Tile& t) {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    tile_rsrc<TK, D * EB>(sg, j, rk, rv);
+#pragma unroll
+    for (int m = 0; m < KS; ++m) t.k[m] = buffer_load16(rk, k_off + 64u * m);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16(rv, v_off + (uint32_t)i * sg.tsb);
+  };
+
+  auto compute_tile = [&](int j, const Tile& t) {
+    const u4_t(&kt)[KS] = t.k;
+    const u4_t(&vt)[4] = t.v;
+    f4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < KS; ++m) s4 = mfma_qk<DT>(kt[m], qb[m], s4);
+    const int64_t kbase = (int64_t)j * TK + 4 * R;
+    float s[4];
+    bool valid[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      valid[r] = kbase + r < nkeys;
+      s[r] = valid[r] ? s4[r] * a.scale_log2 : kNegInf;
+    }
+    const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const bool need = tmax > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // uniform, rare after the first tile
+      float alpha = 1.0f;
+      if (need) {
+        alpha = fast_exp2(m_run - tmax);
+        l_run *= alpha;
+        m_run = tmax;
+      }
+      static_for<GC>([&](auto gi) {
+        constexpr int g = decltype(gi)::value;
+        const float ag = row_bcast<g>(alpha);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+      });
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = valid[r] ? fast_exp2(s[r] - m_run) : 0.0f;
+      l_run += p[r];
+    }
+    const uint32_t P[2] = {pack_pair<DT>(p[0], p[1]), pack_pair<DT>(p[2], p[3])};
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = __builtin_amdgcn_perm(word(vt[2 * pr + 1], w), word(vt[2 * pr], w), 0x05040100u);
+        hi[w] = __builtin_amdgcn_perm(word(vt[2 * pr + 1], w), word(vt[2 * pr], w), 0x07060302u);
+      }
+      static_for<GC>([&](auto gi) {
+        constexpr int g = decltype(gi)::value;
+        const uint32_t pp = row_bcast<g>(P[pr]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[g][2 * w] = pair_dot<DT>(pp, lo[w], acc[g][2 * w]);
+          acc[g][2 * w + 1] = pair_dot<DT>(pp, hi[w], acc[g][2 * w + 1]);
+        }
+      });
+    }
+  };
+
+  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, load_tile, compute_tile);
+
+  // ---- merge the four key groups R of this wave ----
+  float M = m_run;
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+  float lw = l_run * f;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  static_for<GC>([&](auto gi) {
+    constexpr int g = decltype(gi)::value;
+    const float fg = row_bcast<g>(f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[g][e] * fg;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[g][e] = x;
+    }
+  });
+
+  // ---- merge the waves through LDS and write the epilogue ----
+  __shared__ float sm_m[NW][GC];
+  __shared__ float sm_l[NW][GC];
+  __shared__ float sm_acc[NW][GC][D];
+  if (R == 0) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][g][8 * c + e] = acc[g][e];
+    if (c < GC) {
+      sm_m[wave][c] = M;
+      sm_l[wave][c] = lw;
+    }
+  }
+  __syncthreads();
+  store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
+}
+
+// Host-side dispatch over (path, D, rows) for one dtype. The matrix-core
+// kernel exists for 16-bit inputs at head dim 128.
+template <int DT>
+constexpr bool has_mfma_path(int dim) {
+  return DT != DT_F32 && dim == 128;
+}
+
 template <int DT, int D>
-hipError_t launch_split_d(const SplitArgs& a, int rows, dim3 grid, hipStream_t s) {
+hipError_t launch_split_d(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
   dim3 block(kWave * kWavesPerGroup);
+  if constexpr (DT != DT_F32 && D == 128) {
+    if (mfma) {
+      switch (rows) {
+#define FD_CASE(R) \
+  case R: hipLaunchKernelGGL((split_kernel_mfma<DT, R>), grid, block, 0, s, a); break;
+        FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
+#undef FD_CASE
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+  }
   switch (rows) {
 #define FD_CASE(R) \
   case R: hipLaunchKernelGGL((split_kernel<DT, D, R>), grid, block, 0, s, a); break;
@@ -409,12 +680,13 @@ hipError_t launch_split_d(const SplitArgs& a, int rows, dim3 grid, hipStream_t s
 }
 
 template <int DT>
-hipError_t launch_split_dt(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s) {
+hipError_t launch_split_dt(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
+                           hipStream_t s) {
   switch (dim) {
-    case 16: return launch_split_d<DT, 16>(a, rows, grid, s);
-    case 32: return launch_split_d<DT, 32>(a, rows, grid, s);
-    case 64: return launch_split_d<DT, 64>(a, rows, grid, s);
-    case 128: return launch_split_d<DT, 128>(a, rows, grid, s);
+    case 16: return launch_split_d<DT, 16>(a, rows, mfma, grid, s);
+    case 32: return launch_split_d<DT, 32>(a, rows, mfma, grid, s);
+    case 64: return launch_split_d<DT, 64>(a, rows, mfma, grid, s);
+    case 128: return launch_split_d<DT, 128>(a, rows, mfma, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

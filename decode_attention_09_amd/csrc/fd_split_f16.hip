@@ -5,8 +5,9 @@
 
 namespace fd {
 
-hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, dim3 grid, hipStream_t s) {
-  return launch_split_dt<DT_F16>(a, dim, rows, grid, s);
+hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
+                             hipStream_t s) {
+  return launch_split_dt<DT_F16>(a, dim, rows, mfma, grid, s);
 }
 
 }  // namespace fd

@@ -103,9 +103,11 @@ typedef struct fd_kv_layout {
  * Rule (04_flash_decoding.py, demo 4; flash_decode_splitk.py's floor of
  * 256 keys per split; decode_attention_splitkv.py's non-empty rule): among
  * split counts that leave every split >= 1 key and the longest sequence
- * >= 256 keys per split, take the smallest whose workgroup count fills the
- * device's workgroup slots to within 90% of the best fill (wave
- * quantisation), preferring no split when one pass already fills them.
+ * >= 256 keys per split, take the one with the least estimated time, where
+ * the workgroup count is quantised to the compute-unit count (wave
+ * quantisation: every CU runs ceil(workgroups / CUs) rounds, each paying a
+ * fixed per-workgroup cost) and, for unequal lengths, the tail is bounded by
+ * the largest split. Ties go to fewer splits.
  * Returns FD_ERR_EMPTY_SPLIT if some length is < 1, FD_ERR_INVALID_ARG for
  * bad sizes, FD_ERR_HIP if the device query fails.
  */
@@ -120,7 +122,8 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
  *   LSE   [batch, num_splits, heads]       log2(sum_t 2^(s2_t)) of split s,
  *                                           s2_t = scale*log2(e)*q.k_t
  * LSE starts at the first 256-byte boundary after Opart. The shapes follow
- * part_shape / lse_shape of decode_attention_splitkv.py, in fp32.
+ * part_shape / lse_shape of decode_attention_splitkv.py, in fp32. Its
+ * contents before a call do not matter.
  */
 size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits);
 
@@ -137,6 +140,7 @@ size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits);
  *   out           [batch, heads, dim] dtype, fully overwritten.
  *   workspace     fd_workspace_bytes(...) bytes of device memory, or NULL
  *                 when num_splits == 1. Contents on return: the partials.
+ *                 Calls that run concurrently must not share a workspace.
  *   stream        hipStream_t as void*.
  */
 int fd_decode_attention(const void* q, const void* k, const void* v,
@@ -166,6 +170,20 @@ int fd_decode_split(const void* q, const void* k, const void* v,
  */
 int fd_decode_combine(const void* workspace, int batch, int heads, int dim,
                       int num_splits, void* out, void* stream, int dtype);
+
+/*
+ * fd_set_kernel_path -- which split kernel later calls launch, process-wide
+ * (for benchmarks and tests that compare the two; calls already enqueued are
+ * unaffected). FD_PATH_VALU: vector-ALU dot products (v_dot2 / FMA) for
+ * QK^T and PV everywhere. FD_PATH_MFMA: QK^T on the matrix cores
+ * (v_mfma_f32_16x16x32_{f16,bf16}) wherever that kernel exists -- fp16/bf16
+ * at head dim 128 -- and the VALU kernel elsewhere. FD_PATH_AUTO (the
+ * default): the library's measured choice. Both kernels compute the same
+ * function to the same tolerances. Returns the previous setting, or -1
+ * (setting unchanged) for an unknown value.
+ */
+enum { FD_PATH_AUTO = 0, FD_PATH_VALU = 1, FD_PATH_MFMA = 2 };
+int fd_set_kernel_path(int path);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fd_status_string(int status);

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
-              "fd_decode_combine", "fd_status_string", "fd_last_error"):
+              "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path"):
         assert n in names
 
 
@@ -94,24 +94,41 @@ def test_planner_keeps_256_keys_per_split():
 
 
 def test_planner_no_split_when_one_pass_fills_the_device():
-    # 256 x 2 KV heads = 512 workgroups fill 256 CUs x 2 slots in one pass
+    # 256 x 2 KV heads = 512 workgroups already give every one of 256 CUs work
     assert plan(256, 16, 2, 128, [256] * 256) == 1
 
 
 def test_planner_splits_a_single_long_sequence():
-    # 1 sequence x 8 KV heads: one workgroup per head leaves the device idle
+    # 1 sequence x 8 KV heads: one workgroup per head leaves the device idle;
+    # the split count fills the 256 CUs with whole rounds of workgroups
     ns = plan(1, 32, 8, 128, [131072])
     wgs = 8 * ns
-    assert ns > 16 and wgs <= 2 * 256 and wgs >= 0.9 * 512
+    assert ns >= 16 and wgs % 256 == 0
+
+
+def test_planner_quantises_to_the_cu_count():
+    # measured on MI355X: 16/2 heads, batch 8 x 8192 keys is fastest at 16
+    # splits (256 workgroups), batch 1 x 65536 at 128 (256 workgroups)
+    assert plan(8, 16, 2, 128, [8192] * 8) == 16
+    assert plan(1, 16, 2, 128, [65536]) == 128
+
+
+def test_planner_spreads_unequal_lengths():
+    # varlen batch: more, shorter splits than the uniform rule would take,
+    # so the longest sequence does not set the tail
+    import numpy as np
+    lens = np.random.default_rng(0).integers(64, 32769, 32).tolist()
+    ns = plan(32, 28, 4, 128, lens)
+    assert ns >= 8 and ns <= min(lens)
+    assert plan(32, 28, 4, 128, [max(lens)] * 32) <= ns
 
 
 def test_planner_wave_quantisation_example():
-    # 04_flash_decoding.py, demo 4: batch 64, S=2K, 16/2 heads on 108 SMs;
-    # without splitting, 128 CTAs leave the second wave nearly empty, while
-    # 4-16 splits pack the waves. With one resident workgroup per SM:
-    ns = fd.fd_plan_splits(64, 16, 2, 128, fd.FD_F16, [2048] * 64, 54, 0)
-    # (54 CUs x 2 slots = 108 slots, the same slot count as the page's 108 SMs)
-    assert 2 <= ns <= 16
+    # 04_flash_decoding.py, demo 4: batch 64, S=2K, 16/2 heads on 108 SMs
+    # (one CTA resident per SM). Without splitting, 128 CTAs leave the second
+    # wave nearly empty; 4-16 splits pack the waves and the model time drops.
+    ns = fd.fd_plan_splits(64, 16, 2, 128, fd.FD_F16, [2048] * 64, 108, 0)
+    assert 4 <= ns <= 16
     wgs = 128 * ns
     passes = math.ceil(wgs / 108)
     assert wgs / (passes * 108) > 128 / (2 * 108)
@@ -170,3 +187,12 @@ def test_split_and_combine_reject_before_launch():
     assert lib.fd_decode_combine(16, 1, 8, 128, 2, None, None, 1) == 1
     assert lib.fd_decode_combine(16, 1, 8, 96, 2, 16, None, 1) == 2
     assert lib.fd_decode_combine(16, 0, 8, 128, 2, 16, None, 1) == 1
+
+
+def test_kernel_path_setting():
+    prev = fd.fd_set_kernel_path(fd.FD_PATH_VALU)
+    assert fd.fd_set_kernel_path(fd.FD_PATH_MFMA) == fd.FD_PATH_VALU
+    assert fd.fd_set_kernel_path(prev) == fd.FD_PATH_MFMA
+    assert _lib().fd_set_kernel_path(7) == -1
+    with pytest.raises(ValueError):
+        fd.fd_set_kernel_path(9)

@@ -20,6 +20,18 @@ DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 def _gpu():
     H.require_gpu()
     yield
+    H.fd().fd_set_kernel_path(H.fd().FD_PATH_AUTO)
+
+
+@pytest.fixture(params=["valu", "mfma"])
+def kernel_path(request):
+    """Run the test on each split kernel (MFMA falls back to VALU where the
+    matrix-core kernel does not exist)."""
+    fd = H.fd()
+    prev = fd.fd_set_kernel_path({"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[request.param])
+    H.announce("kernel path", request.param)
+    yield request.param
+    fd.fd_set_kernel_path(prev)
 
 
 def _bounds(L, ns):
@@ -84,11 +96,13 @@ CASES = [
     ([100, 37, 64], 32, 2, 128, "f16", 37, "packed"),   # group 16: two row chunks
     ([3, 10, 5], 8, 1, 64, "f16", 7, "packed"),         # ns > some lengths: empty splits
     ([0, 12, 40], 8, 2, 128, "bf16", 4, "packed"),      # an empty sequence
+    ([1, 15, 16, 17, 33, 4099], 16, 2, 128, "bf16", 3, "packed"),
+    ([2000, 7, 64], 24, 4, 128, "f16", 5, "bhsd"),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[4]}-d{c[3]}-g{c[1]//c[2]}-ns{c[5]}-{c[6]}")
-def test_split_bounds_and_varlen_indexing_are_exact(case):
+def test_split_bounds_and_varlen_indexing_are_exact(case, kernel_path):
     lengths, heads, kv_heads, dim, dtype, ns, layout = case
     inp = structured_inputs(lengths, heads, kv_heads, dim, dtype, ns, layout)
     G = heads // kv_heads
@@ -126,7 +140,7 @@ def _rand_inputs(lengths, heads, kv_heads, dim, dtype, layout="packed", seed=0, 
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_single_key_returns_its_value_exactly(dtype):
+def test_single_key_returns_its_value_exactly(dtype, kernel_path):
     inp = _rand_inputs([1, 1, 1], 8, 2, 128, dtype)
     out = H.gpu_attention(inp, 1)
     G = 4
@@ -146,7 +160,7 @@ def test_empty_sequence_gives_zero_rows():
 
 
 @pytest.mark.parametrize("layout", ["packed", "bhsd"])
-def test_nan_outside_sequences_is_never_read(layout):
+def test_nan_outside_sequences_is_never_read(layout, kernel_path):
     inp = _rand_inputs([1, 77, 200, 5], 16, 2, 128, "f16", layout=layout, pad=64)
     for ns in (1, 5):
         out = H.host(H.gpu_attention(inp, ns))
@@ -156,8 +170,9 @@ def test_nan_outside_sequences_is_never_read(layout):
 
 
 @pytest.mark.parametrize("group,kv_heads", [(16, 2), (64, 1), (9, 3), (12, 1)])
-def test_groups_larger_than_one_pass(group, kv_heads):
-    inp = _rand_inputs([300, 1025], group * kv_heads, kv_heads, 64, "bf16")
+@pytest.mark.parametrize("dim", [64, 128])
+def test_groups_larger_than_one_pass(group, kv_heads, dim, kernel_path):
+    inp = _rand_inputs([300, 1025], group * kv_heads, kv_heads, dim, "bf16")
     for ns in (1, 4):
         out = H.host(H.gpu_attention(inp, ns))
         assert H.max_err(out, H.oracle_full(inp, ns)) <= H.TOL["bf16"]
@@ -173,7 +188,7 @@ def test_non_default_scales(scale):
     assert H.max_err(out2, H.oracle_full(inp2, 3, scale=scale)) <= H.TOL["f32"]
 
 
-def test_repeat_calls_are_bitwise_identical():
+def test_repeat_calls_are_bitwise_identical(kernel_path):
     inp = _rand_inputs([5000, 3000], 28, 4, 128, "f16")
     a = H.gpu_attention(inp, 8).clone()
     b = H.gpu_attention(inp, 8).clone()
@@ -221,7 +236,7 @@ GRID_LENS = [1, 37, 64, 65, 300, 1029]
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("dim", [16, 32, 64, 128])
 @pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_grid_dims_dtypes_groups(dtype, dim, group):
+def test_grid_dims_dtypes_groups(dtype, dim, group, kernel_path):
     """Ragged lengths spanning one to many tiles, two KV heads, ns=1 and a
     split count that cuts tiles mid-way."""
     inp = _rand_inputs(GRID_LENS, 2 * group, 2, dim, dtype, seed=group * 7 + dim)
@@ -230,3 +245,27 @@ def test_grid_dims_dtypes_groups(dtype, dim, group):
         out = H.host(H.gpu_attention(inp, ns))
         err = H.max_err(out, ref)
         assert err <= H.TOL[dtype], (dtype, dim, group, ns, err)
+
+
+@pytest.mark.parametrize("lens,heads,kvh,dim,dt,ns", [
+    ([4096] * 4, 32, 32, 128, "f16", 16),           # MHA, 2048 workgroups
+    ([65536], 16, 2, 128, "f16", 128),              # 256 workgroups on 2 groups
+    ([777, 30000, 64, 5000], 28, 4, 128, "bf16", 8),
+    ([3000, 100], 8, 1, 64, "f32", 37),
+])
+def test_whole_call_matches_split_then_combine_over_many_calls(lens, heads, kvh, dim, dt, ns,
+                                                              kernel_path):
+    """Fifty whole calls on one workspace are bitwise equal to the split and
+    combine launches made separately."""
+    fd = H.fd()
+    inp = _rand_inputs(lens, heads, kvh, dim, dt)
+    ws2 = fd.fd_decode_split(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns)
+    ref = torch.empty_like(inp.q)
+    fd.fd_decode_combine(ws2, len(lens), heads, dim, ns, ref)
+    ws = torch.empty(fd.fd_workspace_bytes(len(lens), heads, dim, ns), dtype=torch.uint8,
+                     device=H.DEV)
+    outs = [fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns, workspace=ws)
+            for _ in range(50)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)

@@ -95,19 +95,36 @@ def test_llama_long_context(batch, kv_len):
     torch.cuda.empty_cache()
 
 
-def test_llama_split_sweep():
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_llama_split_sweep(path):
     """batch 1, 64K keys, ns in {1, 2, ..., 128}: every split count gives the
-    oracle's result."""
-    w = W.llama(1, 65536)
-    inp = W.make_inputs(w, H.DEV)
-    ref = H.oracle_full(inp)
-    outs = []
-    for ns in W.LLAMA_SWEEP_SPLITS:
-        out = H.host(H.gpu_attention(inp, ns))
-        err = H.max_err(out, ref)
-        print(f"  ns={ns} err={err:.3e}", flush=True)
-        assert err <= H.TOL["bf16"], (ns, err)
-        outs.append(out)
+    oracle's result, on both split kernels."""
+    fd = H.fd()
+    prev = fd.fd_set_kernel_path({"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[path])
+    try:
+        w = W.llama(1, 65536)
+        inp = W.make_inputs(w, H.DEV)
+        ref = H.oracle_full(inp)
+        for ns in W.LLAMA_SWEEP_SPLITS:
+            out = H.host(H.gpu_attention(inp, ns))
+            err = H.max_err(out, ref)
+            print(f"  {path} ns={ns} err={err:.3e}", flush=True)
+            assert err <= H.TOL["bf16"], (ns, err)
+    finally:
+        fd.fd_set_kernel_path(prev)
+
+
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_varlen_both_kernels(path):
+    """The varlen GQA workload (group 7) on each split kernel explicitly."""
+    fd = H.fd()
+    prev = fd.fd_set_kernel_path({"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[path])
+    try:
+        w = W.varlen_qwen()
+        inp = W.make_inputs(w, H.DEV)
+        check_full(inp, W.varlen_splits(w, inp.lengths))
+    finally:
+        fd.fd_set_kernel_path(prev)
 
 
 def test_varlen_packed_gqa():
