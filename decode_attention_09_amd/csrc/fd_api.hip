@@ -118,6 +118,7 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.sh = L.head_stride;
   a.st = L.token_stride;
   a.scu = L.cu_stride;
+  a.batch = batch;
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.group = sz.group;

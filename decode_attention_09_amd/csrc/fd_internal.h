@@ -8,8 +8,12 @@
 namespace fd {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kWavesPerGroup = 4;  // waves per split workgroup
+#ifndef FD_WAVES_PER_GROUP
+#define FD_WAVES_PER_GROUP 4
+#endif
+constexpr int kWavesPerGroup = FD_WAVES_PER_GROUP;  // waves per split workgroup
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
+constexpr int kLptMaxBatch = 64;   // batches up to this size run longest sequence first
 constexpr int kLoadsPerTile = 4;   // 16-byte K (and V) loads per lane per tile
 #ifndef FD_PREFETCH_TILES
 #define FD_PREFETCH_TILES 1
@@ -27,7 +31,7 @@ struct SplitArgs {
   float* lse;       // [B, ns, H]   fp32 (workspace mode)
   void* out;        // [B, H, D] dtype (direct mode, ns == 1)
   int64_t sb, sh, st, scu;  // K/V strides in elements: batch, head, token, cu
-  int heads, kv_heads, group, num_splits, row_chunks;
+  int batch, heads, kv_heads, group, num_splits, row_chunks;
   int direct;       // 1: write out in dtype; 0: write opart/lse
   float scale_log2; // scale * log2(e)
 };

@@ -158,8 +158,27 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 
 // ------------------------------------------------------- work decoding --
 // Where one split workgroup works: workgroup -> (split, KV head, row chunk,
-// sequence), split index fastest; varlen bounds from cu_seqlens_k and the
-// proportional segment [L*s/ns, L*(s+1)/ns) with 64-bit products.
+// sequence rank), split index fastest; varlen bounds from cu_seqlens_k and
+// the proportional segment [L*s/ns, L*(s+1)/ns) with 64-bit products.
+//
+// Workgroups are dispatched roughly in index order, so for batches of up to
+// kLptMaxBatch sequences the r-th block of workgroups takes the r-th longest
+// sequence (ties by index): long segments start first and short ones fill
+// the tail (longest-processing-time order). Every wave ranks the lengths
+// itself: lane l holds L_l and counts the sequences that precede it; the
+// lane whose rank is r names the sequence. Equal lengths keep index order.
+__device__ __forceinline__ int sequence_of_rank(const int32_t* cu, int batch, int r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int len = -1;
+  if (lane < batch) len = cu[lane + 1] - cu[lane];
+  int rank = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && rank == r);
+  return hit ? (int)__builtin_ctzll(hit) : r;
+}
 struct Segment {
   int b, sid, kvh, h0, nrows;
   int64_t nkeys;
@@ -177,7 +196,8 @@ __device__ __forceinline__ Segment locate_segment(const SplitArgs& a) {
   wg /= ns;
   const int hcn = a.kv_heads * a.row_chunks;
   const int hc = wg % hcn;
-  g.b = wg / hcn;
+  const int rank = wg / hcn;
+  g.b = a.batch <= kLptMaxBatch ? sequence_of_rank(a.cu, a.batch, rank) : rank;
   g.kvh = hc / a.row_chunks;
   const int chunk = hc % a.row_chunks;
   g.h0 = g.kvh * a.group + chunk * kMaxRowsPerPass;
