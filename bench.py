@@ -15,6 +15,7 @@ launches right after the timed steps) and the CPU oracle's rate on the same
 workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+    python bench.py --workload NAME[,NAME...] --sweep-splits 1,2,4,8 [--kernel-path P]
 """
 from __future__ import annotations
 
@@ -123,8 +124,14 @@ def cpu_baseline(inp, ns, budget_s: float):
     }
 
 
+def split_workgroups(w, ns: int, rows_per_workgroup: int) -> int:
+    """Workgroups of the split launch: one per (sequence, KV head, block of
+    up to rows_per_workgroup query heads of the group, split)."""
+    return w.batch * w.kv_heads * math.ceil(w.group / rows_per_workgroup) * ns
+
+
 def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES,
-        ns_override: int = 0):
+        ns_override: int = 0, rows_per_workgroup: int = 8):
     import torch
     import workloads as W
     import decode_attention_09_amd as fd
@@ -191,7 +198,9 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
         "data": "synthetic (seeded N(0,1) q/K/V, no model weights)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
                    "kv_heads": w.kv_heads, "head_dim": w.dim, "kv_len_total": sum(inp.lengths),
-                   "layout": w.layout, "num_splits": ns, "kv_bytes": kv_bytes,
+                   "layout": w.layout, "num_splits": ns,
+                   "split_workgroups": split_workgroups(w, ns, rows_per_workgroup),
+                   "kv_bytes": kv_bytes,
                    "kv_copies_rotated": copies, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
@@ -229,8 +238,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--num-splits", type=int, default=0,
                     help="override the workload's split count (sweeps)")
-    ap.add_argument("--kernel-path", choices=["auto", "valu", "mfma"], default="auto",
-                    help="split kernel variant (default: the library's own choice)")
+    ap.add_argument("--kernel-path", choices=["auto", "valu", "mfma", "unpacked"],
+                    default="auto",
+                    help="split kernel variant (default: the library's own choice; "
+                         "unpacked = one query head per workgroup, the comparison path)")
+    ap.add_argument("--sweep-splits", default="",
+                    help="comma-separated split counts: one line (no CPU leg) per "
+                         "workload in --workload (comma-separated) and split count")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 10 times (reference for the "
                          "FETCH_SIZE/WRITE_SIZE counters)")
@@ -244,18 +258,26 @@ def main():
         sys.exit(2)
     import decode_attention_09_amd as fd
     fd.fd_set_kernel_path({"auto": fd.FD_PATH_AUTO, "valu": fd.FD_PATH_VALU,
-                           "mfma": fd.FD_PATH_MFMA}[args.kernel_path])
-    if args.all:
+                           "mfma": fd.FD_PATH_MFMA,
+                           "unpacked": fd.FD_PATH_UNPACKED}[args.kernel_path])
+    rows = 1 if args.kernel_path == "unpacked" else 8
+    if args.all or args.sweep_splits:
+        import torch
         import workloads as W
-        for w in W.all_workloads():
-            r = run(w, args.steps, args.warmup, 0.0)
+        if args.all:
+            todo = [(w, args.num_splits) for w in W.all_workloads()]
+        else:
+            splits = [int(x) for x in args.sweep_splits.split(",") if x]
+            todo = [(workload_by_name(n), ns) for n in args.workload.split(",")
+                    for ns in splits]
+        for w, ns in todo:
+            r = run(w, args.steps, args.warmup, 0.0, ns_override=ns, rows_per_workgroup=rows)
             r["kernel_path"] = args.kernel_path
             print(json.dumps(r), flush=True)
-            import torch
             torch.cuda.empty_cache()
         return
     r = run(workload_by_name(args.workload), args.steps, args.warmup, args.cpu_seconds,
-            ns_override=args.num_splits)
+            ns_override=args.num_splits, rows_per_workgroup=rows)
     r["kernel_path"] = args.kernel_path
     print(json.dumps(r), flush=True)
 

@@ -16,12 +16,12 @@ __all__ = [
     "FD_F32", "FD_F16", "FD_BF16", "FD_MAX_SPLITS", "FdError", "library_path", "load_library",
     "fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
     "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path", "kv_layout",
-    "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "workspace_views",
+    "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "FD_PATH_UNPACKED", "workspace_views",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_MAX_SPLITS = 16384
-FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA = 0, 1, 2
+FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA, FD_PATH_UNPACKED = 0, 1, 2, 3
 _STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
            3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP"}
 
@@ -100,8 +100,8 @@ def fd_last_error() -> str:
 
 
 def fd_set_kernel_path(path: int) -> int:
-    """Select the split kernel (FD_PATH_AUTO / _VALU / _MFMA); returns the
-    previous setting."""
+    """Select the split kernel (FD_PATH_AUTO / _VALU / _MFMA / _UNPACKED);
+    returns the previous setting."""
     prev = load_library().fd_set_kernel_path(int(path))
     if prev < 0:
         raise ValueError(f"unknown kernel path {path}")

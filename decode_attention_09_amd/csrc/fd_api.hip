@@ -49,6 +49,29 @@ constexpr int kPlanMinKeysPerSplit = 256;
 // MI355X: about 1 us at ~25-30 GB/s per CU).
 constexpr double kPlanWorkgroupBytes = 32.0 * 1024.0;
 
+// Compute units of the current device, cached per device ordinal.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return FD_OK;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return FD_OK;
+}
+
 int elem_bytes(int dtype) { return dtype == FD_F32 ? 4 : 2; }
 
 bool dim_ok(int dim) { return dim == 16 || dim == 32 || dim == 64 || dim == 128; }
@@ -60,9 +83,13 @@ struct Sizes {
   int64_t workgroups;
 };
 
+// Query rows of a GQA group one workgroup handles: up to 8 (the packed
+// group), or 1 for the unpacked comparison path.
+int rows_per_pass(int path) { return path == FD_PATH_UNPACKED ? 1 : fd::kMaxRowsPerPass; }
+
 // Checks shared by every launching entry point.
 int check_common(int batch, int heads, int kv_heads, int dim, int num_splits, int dtype,
-                 Sizes* sz) {
+                 Sizes* sz, int max_rows = fd::kMaxRowsPerPass) {
   if (batch < 1 || heads < 1 || kv_heads < 1 || num_splits < 1) return FD_ERR_INVALID_ARG;
   if (heads % kv_heads != 0) return FD_ERR_INVALID_ARG;
   if (num_splits > FD_MAX_SPLITS) return FD_ERR_INVALID_ARG;
@@ -71,8 +98,8 @@ int check_common(int batch, int heads, int kv_heads, int dim, int num_splits, in
   const int group = heads / kv_heads;
   if (group > FD_MAX_GROUP) return FD_ERR_UNSUPPORTED;
   sz->group = group;
-  sz->rows = group < fd::kMaxRowsPerPass ? group : fd::kMaxRowsPerPass;
-  sz->row_chunks = (group + fd::kMaxRowsPerPass - 1) / fd::kMaxRowsPerPass;
+  sz->rows = group < max_rows ? group : max_rows;
+  sz->row_chunks = (group + max_rows - 1) / max_rows;
   sz->workgroups = (int64_t)batch * kv_heads * sz->row_chunks * num_splits;
   if (sz->workgroups > kMaxWorkgroups) return FD_ERR_INVALID_ARG;
   if ((int64_t)batch * heads > INT_MAX / 2) return FD_ERR_INVALID_ARG;
@@ -105,7 +132,7 @@ int check_layout(const fd_kv_layout* lay, int kv_heads, int dim, int dtype, fd_k
 int launch_split(const void* q, const void* k, const void* v, const int32_t* cu, int batch,
                  int heads, int kv_heads, int dim, int num_splits, float scale, float* opart,
                  float* lse, void* out, int direct, hipStream_t stream, int dtype,
-                 const fd_kv_layout& L, const Sizes& sz) {
+                 const fd_kv_layout& L, const Sizes& sz, int path) {
   fd::SplitArgs a;
   a.q = q;
   a.k = k;
@@ -124,10 +151,10 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.group = sz.group;
   a.num_splits = num_splits;
   a.row_chunks = sz.row_chunks;
+  a.rows_per_pass = sz.rows;
   a.direct = direct;
   a.scale_log2 = (float)((double)scale * kLog2e);
   dim3 grid((unsigned)sz.workgroups);
-  const int path = g_path.load(std::memory_order_relaxed);
   const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;
   switch (dtype) {
@@ -179,11 +206,8 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
   if (min_len < 1) return FD_ERR_EMPTY_SPLIT;
   if (num_cus < 0) return FD_ERR_INVALID_ARG;
   if (num_cus == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    const int st2 = device_cus(&num_cus);
+    if (st2 != FD_OK) return st2;
   }
   if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
   // candidates: every split non-empty, the longest sequence keeps
@@ -229,8 +253,9 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
 int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
                     int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
                     void* workspace, void* stream, int dtype, const fd_kv_layout* layout) {
+  const int path = g_path.load(std::memory_order_relaxed);
   Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz);
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
   if (st != FD_OK) return st;
   if (!q || !k || !v || !cu_seqlens_k || !workspace) return FD_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
@@ -243,7 +268,7 @@ int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* 
   float* opart = reinterpret_cast<float*>(ws);
   float* lse = reinterpret_cast<float*>(ws + lse_offset(batch, heads, dim, num_splits));
   return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
-                      opart, lse, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz);
+                      opart, lse, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path);
 }
 
 int fd_decode_combine(const void* workspace, int batch, int heads, int dim, int num_splits,
@@ -271,8 +296,9 @@ int fd_decode_attention(const void* q, const void* k, const void* v, const int32
                         int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
                         void* out, void* workspace, void* stream, int dtype,
                         const fd_kv_layout* layout) {
+  const int path = g_path.load(std::memory_order_relaxed);
   Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz);
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
   if (st != FD_OK) return st;
   if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
   if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
@@ -285,7 +311,7 @@ int fd_decode_attention(const void* q, const void* k, const void* v, const int32
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (num_splits == 1) {
     return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, nullptr,
-                        nullptr, out, 1, s, dtype, L, sz);
+                        nullptr, out, 1, s, dtype, L, sz, path);
   }
   st = fd_decode_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
                        workspace, stream, dtype, layout);
@@ -307,7 +333,9 @@ const char* fd_status_string(int status) {
 const char* fd_last_error(void) { return g_last_error; }
 
 int fd_set_kernel_path(int path) {
-  if (path != FD_PATH_AUTO && path != FD_PATH_VALU && path != FD_PATH_MFMA) return -1;
+  if (path != FD_PATH_AUTO && path != FD_PATH_VALU && path != FD_PATH_MFMA &&
+      path != FD_PATH_UNPACKED)
+    return -1;
   return g_path.exchange(path);
 }
 

@@ -11,22 +11,15 @@ namespace fd {
 // the combine segment of gqa_decode_splitkv in "decode_attention_splitkv.py"
 // (TileLang tutorial, ch. 18), with the weight of split s for a head applied
 // to that head's row, and the merge of "04_flash_decoding.py" (CS349E
-// lecture 11), demo 1. Every thread first helps reduce the LSEs through
-// LDS; then each wave streams a strided subset of the partial rows (SPW rows
-// side by side, D/64 dims per lane when D >= 64) and the waves' sums meet in
-// LDS. All threads of the workgroup must call it (it synchronises).
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int mask = 1; mask < kWave; mask <<= 1) x = fmaxf(x, __shfl_xor(x, mask));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int mask = 1; mask < kWave; mask <<= 1) x += __shfl_xor(x, mask);
-  return x;
-}
-
+// lecture 11), demo 1.
+//
+// Each wave owns a strided subset of the partial rows (SPW rows side by
+// side, D/64 dims per lane when D >= 64). Every load the merge needs is
+// issued up front -- one LSE per thread for the max and the sum, and the
+// first KR partial rows of each lane group with their LSEs -- so the whole
+// merge waits for memory once; rows beyond KR (many splits) are read after
+// the reductions. The waves' maxima, sums and row sums meet in LDS. All
+// threads of the workgroup must call it (it synchronises).
 template <int DT, int D, int NWAVES>
 __device__ __forceinline__ void combine_head(const float* opart, const float* lse_base, void* out,
                                              int heads, int ns, int b, int h) {
@@ -35,6 +28,7 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
   constexpr int LPS = D / DPL;                     // lanes per partial row
   constexpr int SPW = kWave / LPS;                 // rows a wave reads side by side
   constexpr int RPG = SPW * NWAVES;                // rows the group reads side by side
+  constexpr int KR = 8;                            // rows per lane group held in registers
   __shared__ float red[NWAVES];
   __shared__ float part[NWAVES][D];
 
@@ -44,10 +38,25 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
   const int64_t bh = (int64_t)b * heads + h;
   const float* lse = lse_base + (int64_t)b * ns * heads + h;  // split stride = heads
   const float* op = opart + bh * ns * D;
+  const int sg = lane / LPS;
+  const int dl = lane % LPS;
+  const int s0 = wave * SPW + sg;  // first partial row of this lane group
 
-  float mx = kNegInf;
-  for (int s = tid; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * heads]);
-  mx = wave_max(mx);
+  // every load up front
+  const float l_own = tid < ns ? lse[(int64_t)tid * heads] : kNegInf;
+  float pl[KR], pv[KR][DPL];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int s = s0 + k * RPG;
+    const bool in = s < ns;
+    pl[k] = in ? lse[(int64_t)s * heads] : kNegInf;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) pv[k][e] = in ? op[(int64_t)s * D + dl * DPL + e] : 0.0f;
+  }
+
+  float mx = l_own;
+  for (int s = tid + NT; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * heads]);
+  mx = across_groups<1>(mx, OpMax{});
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   mx = red[0];
@@ -55,23 +64,27 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
   for (int w = 1; w < NWAVES; ++w) mx = fmaxf(mx, red[w]);
   __syncthreads();
 
-  const int sg = lane / LPS;
-  const int dl = lane % LPS;
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
 
   if (mx != kNegInf) {  // uniform: every split empty -> zero row
-    float tot = 0.0f;
-    for (int s = tid; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * heads] - mx);
-    tot = wave_sum(tot);
+    float tot = l_own == kNegInf ? 0.0f : fast_exp2(l_own - mx);
+    for (int s = tid + NT; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * heads] - mx);
+    tot = across_groups<1>(tot, OpAdd{});
     if (lane == 0) red[wave] = tot;
     __syncthreads();
     tot = 0.0f;
 #pragma unroll
     for (int w = 0; w < NWAVES; ++w) tot += red[w];
     const float lse_all = mx + fast_log2(tot);
-    int s = wave * SPW + sg;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const float wt = fast_exp2(pl[k] - lse_all);  // 0 for rows past ns
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(wt, pv[k][e], acc[e]);
+    }
+    int s = s0 + KR * RPG;
     for (; s + 3 * RPG < ns; s += 4 * RPG) {
       float wt[4];
       float v[4][DPL];
@@ -95,9 +108,7 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
     }
   }
 #pragma unroll
-  for (int mask = LPS; mask < kWave; mask <<= 1)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] += __shfl_xor(acc[e], mask);
+  for (int e = 0; e < DPL; ++e) acc[e] = across_groups<LPS>(acc[e], OpAdd{});
   if (sg == 0) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) part[wave][dl * DPL + e] = acc[e];
@@ -121,15 +132,20 @@ __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineAr
                                      bh / a.heads, bh % a.heads);
 }
 
-template <int DT>
-static hipError_t launch_combine_dt(const CombineArgs& a, int dim, hipStream_t s) {
+template <int DT, int D>
+static void launch_combine_d(const CombineArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.batch * a.heads));
   dim3 block(kWave * kCombineWaves);
+  hipLaunchKernelGGL((combine_kernel<DT, D>), grid, block, 0, s, a);
+}
+
+template <int DT>
+static hipError_t launch_combine_dt(const CombineArgs& a, int dim, hipStream_t s) {
   switch (dim) {
-    case 16: hipLaunchKernelGGL((combine_kernel<DT, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((combine_kernel<DT, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((combine_kernel<DT, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<DT, 128>), grid, block, 0, s, a); break;
+    case 16: launch_combine_d<DT, 16>(a, s); break;
+    case 32: launch_combine_d<DT, 32>(a, s); break;
+    case 64: launch_combine_d<DT, 64>(a, s); break;
+    case 128: launch_combine_d<DT, 128>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

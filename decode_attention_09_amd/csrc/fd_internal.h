@@ -32,6 +32,7 @@ struct SplitArgs {
   void* out;        // [B, H, D] dtype (direct mode, ns == 1)
   int64_t sb, sh, st, scu;  // K/V strides in elements: batch, head, token, cu
   int batch, heads, kv_heads, group, num_splits, row_chunks;
+  int rows_per_pass; // query rows of a group per workgroup (<= the kernel's rows)
   int direct;       // 1: write out in dtype; 0: write opart/lse
   float scale_log2; // scale * log2(e)
 };

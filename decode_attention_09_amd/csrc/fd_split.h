@@ -62,6 +62,30 @@ __device__ __forceinline__ float dpp_mov(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Pairwise combine of 16-lane rows (0<->1, 2<->3) or of 32-lane halves with
+// v_permlane16_swap / v_permlane32_swap: both lanes of a pair receive the
+// two values in the same order, so op gives them bitwise equal results.
+struct OpAdd {
+  __device__ float operator()(float x, float y) const { return x + y; }
+};
+struct OpMax {
+  __device__ float operator()(float x, float y) const { return fmaxf(x, y); }
+};
+
+template <typename Op>
+__device__ __forceinline__ float rows_pair(float x, Op op) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return op(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+template <typename Op>
+__device__ __forceinline__ float halves_pair(float x, Op op) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return op(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 // Sum over aligned groups of LPR lanes; every lane of a group gets the same
 // (bitwise) result because each butterfly step adds the same two values.
 template <int LPR>
@@ -70,7 +94,22 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
   if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
   if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror
-  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPR >= 32) x = rows_pair(x, OpAdd{});
+  return x;
+}
+
+// Reduce across the 64/LPR lane groups of a wave: lanes with the same
+// lane % LPR combine. Within a 16-lane row the groups are folded by DPP
+// row rotations (lane i takes i + n mod 16), then rows and halves by the
+// swaps. Every lane receives the reduction of its residue class.
+template <int LPR, typename Op>
+__device__ __forceinline__ float across_groups(float x, Op op) {
+  if constexpr (LPR <= 1) x = op(x, dpp_mov<0x121>(x));  // row_ror:1
+  if constexpr (LPR <= 2) x = op(x, dpp_mov<0x122>(x));  // row_ror:2
+  if constexpr (LPR <= 4) x = op(x, dpp_mov<0x124>(x));  // row_ror:4
+  if constexpr (LPR <= 8) x = op(x, dpp_mov<0x128>(x));  // row_ror:8
+  if constexpr (LPR <= 16) x = rows_pair(x, op);
+  if constexpr (LPR <= 32) x = halves_pair(x, op);
   return x;
 }
 
@@ -157,28 +196,67 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 }
 
 // ------------------------------------------------------- work decoding --
-// Where one split workgroup works: workgroup -> (split, KV head, row chunk,
-// sequence rank), split index fastest; varlen bounds from cu_seqlens_k and
-// the proportional segment [L*s/ns, L*(s+1)/ns) with 64-bit products.
+// One workgroup per segment ("item"): workgroup -> (split, KV head, row
+// chunk, sequence rank), split index fastest, without memory access; then
+// the sequence, its varlen bounds and the proportional segment.
 //
 // Workgroups are dispatched roughly in index order, so for batches of up to
-// kLptMaxBatch sequences the r-th block of workgroups takes the r-th longest
-// sequence (ties by index): long segments start first and short ones fill
-// the tail (longest-processing-time order). Every wave ranks the lengths
-// itself: lane l holds L_l and counts the sequences that precede it; the
-// lane whose rank is r names the sequence. Equal lengths keep index order.
-__device__ __forceinline__ int sequence_of_rank(const int32_t* cu, int batch, int r) {
+// kLptMaxBatch sequences rank r is the r-th longest sequence (ties by
+// index): long segments start first and short ones fill the tail
+// (longest-processing-time order). With equal lengths the order is the
+// identity, so a workgroup loads its q rows for sequence `rank` while
+// cu_seqlens_k is in flight and reloads them only in a varlen batch.
+struct WorkItem {
+  int sid, kvh, rank, h0, nrows;
+};
+
+template <int GC>
+__device__ __forceinline__ WorkItem decode_item(const SplitArgs& a, int item) {
+  WorkItem w;
+  w.sid = item % a.num_splits;
+  item /= a.num_splits;
+  const int hcn = a.kv_heads * a.row_chunks;
+  const int hc = item % hcn;
+  w.rank = item / hcn;
+  w.kvh = hc / a.row_chunks;
+  const int chunk = hc % a.row_chunks;
+  w.h0 = w.kvh * a.group + chunk * a.rows_per_pass;
+  w.nrows = min(GC, a.group - chunk * a.rows_per_pass);
+  return w;
+}
+
+// Per-lane view of cu_seqlens_k for batches of up to kLptMaxBatch
+// sequences, one load per lane: lane l < batch holds cu[l], cu[l+1] and the
+// LPT rank of sequence l (lanes past the batch: rank -1). Each wave ranks
+// the lengths itself; an all-equal batch skips the ranking.
+struct LaneSeqs {
+  int lo, hi, rank;
+};
+
+__device__ __forceinline__ LaneSeqs lane_seqs(const SplitArgs& a) {
+  LaneSeqs s{0, 0, -1};
+  if (a.batch > kLptMaxBatch) return s;
   const int lane = threadIdx.x & (kWave - 1);
-  int len = -1;
-  if (lane < batch) len = cu[lane + 1] - cu[lane];
+  const bool mine = lane < a.batch;
+  if (mine) {
+    s.lo = a.cu[lane];
+    s.hi = a.cu[lane + 1];
+  }
+  const int len = mine ? s.hi - s.lo : -1;
+  const int len0 = __builtin_amdgcn_readfirstlane(len);
+  if (__builtin_amdgcn_ballot_w64(mine && len != len0) == 0) {
+    s.rank = mine ? lane : -1;
+    return s;
+  }
   int rank = 0;
-  for (int j = 0; j < batch; ++j) {
+  for (int j = 0; j < a.batch; ++j) {
     const int lj = __builtin_amdgcn_readlane(len, j);
     rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
   }
-  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && rank == r);
-  return hit ? (int)__builtin_ctzll(hit) : r;
+  s.rank = mine ? rank : -1;
+  return s;
 }
+
 struct Segment {
   int b, sid, kvh, h0, nrows;
   int64_t nkeys;
@@ -187,23 +265,28 @@ struct Segment {
   uint32_t tsb;    // bytes between consecutive keys
 };
 
-template <int EB, int GC>
-__device__ __forceinline__ Segment locate_segment(const SplitArgs& a) {
+// The sequence, its varlen bounds and the proportional segment
+// [L*s/ns, L*(s+1)/ns) (64-bit products) of an item.
+template <int EB>
+__device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const WorkItem& w,
+                                                  const LaneSeqs& ls) {
   Segment g;
-  int wg = blockIdx.x;
+  g.sid = w.sid;
+  g.kvh = w.kvh;
+  g.h0 = w.h0;
+  g.nrows = w.nrows;
+  int cu0, cu1;
+  if (a.batch <= kLptMaxBatch) {
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(ls.rank == w.rank);
+    g.b = hit ? (int)__builtin_ctzll(hit) : w.rank;
+    cu0 = __builtin_amdgcn_readlane(ls.lo, g.b);
+    cu1 = __builtin_amdgcn_readlane(ls.hi, g.b);
+  } else {
+    g.b = w.rank;
+    cu0 = a.cu[g.b];
+    cu1 = a.cu[g.b + 1];
+  }
   const int ns = a.num_splits;
-  g.sid = wg % ns;
-  wg /= ns;
-  const int hcn = a.kv_heads * a.row_chunks;
-  const int hc = wg % hcn;
-  const int rank = wg / hcn;
-  g.b = a.batch <= kLptMaxBatch ? sequence_of_rank(a.cu, a.batch, rank) : rank;
-  g.kvh = hc / a.row_chunks;
-  const int chunk = hc % a.row_chunks;
-  g.h0 = g.kvh * a.group + chunk * kMaxRowsPerPass;
-  g.nrows = min(GC, a.group - chunk * kMaxRowsPerPass);
-  const int cu0 = a.cu[g.b];
-  const int cu1 = a.cu[g.b + 1];
   const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
   const int64_t seg0 = L * g.sid / ns;
   g.nkeys = L * (g.sid + 1) / ns - seg0;
@@ -272,18 +355,20 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// A wave's walk over the tiles first, first+NW, ... (< nt) of its segment
+// A wave's walk over the tiles first, first+NW, ... (< nt) of a segment
 // with PF tiles' loads in flight while it computes one: PF+1 register
 // buffers used round-robin, the loop unrolled so every buffer index is a
-// constant. Loads of tiles past the segment are harmless (empty
-// descriptors); the walk stops after the last tile. The scheduling barriers
-// keep each prefetch ahead of the compute it overlaps.
+// constant. The caller has already issued the load of tile `first` into
+// buf[0]. Loads of tiles past the segment are harmless (empty descriptors
+// return zeros without touching memory; skipping them costs registers);
+// the walk stops after the last tile. The
+// scheduling barriers keep each prefetch ahead of the compute it overlaps.
 template <int PF, int NW, typename Tile, typename Load, typename Compute>
-__device__ __forceinline__ void tile_pipeline(int first, int nt, Load&& load, Compute&& compute) {
+__device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF + 1], Load&& load,
+                                              Compute&& compute) {
   if (first >= nt) return;  // uniform: this wave has no tile of the segment
-  Tile buf[PF + 1];
-  static_for<PF>([&](auto ui) {
-    constexpr int u = decltype(ui)::value;
+  static_for<PF - 1>([&](auto ui) {
+    constexpr int u = decltype(ui)::value + 1;
     load(first + u * NW, buf[u]);
   });
   int j = first;
@@ -324,54 +409,44 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
   const int rg = lane / LPR;  // which row of a load this lane holds
   const int c = lane % LPR;   // which 16-byte chunk of the row
 
-  const Segment sg = locate_segment<EB, GC>(a);
-  const int64_t nkeys = sg.nkeys;
-
-  // q chunks of the packed rows (rows past the group read as zero)
+  const LaneSeqs ls = lane_seqs(a);
+  // q chunks of the packed rows of the current item (rows past the group
+  // read as zero)
   u4_t q[GC];
+  auto load_q = [&](const WorkItem& w, int b) {
 #pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    if (g < sg.nrows) {
-      const char* qp = static_cast<const char*>(a.q) +
-                       (((int64_t)sg.b * a.heads + sg.h0 + g) * D + c * EPL) * EB;
-      q[g] = *reinterpret_cast<const u4_t*>(qp);
-    } else {
-      q[g] = u4_t{0u, 0u, 0u, 0u};
+    for (int g = 0; g < GC; ++g) {
+      if (g < w.nrows) {
+        const char* qp = static_cast<const char*>(a.q) +
+                         (((int64_t)b * a.heads + w.h0 + g) * D + c * EPL) * EB;
+        q[g] = *reinterpret_cast<const u4_t*>(qp);
+      } else {
+        q[g] = u4_t{0u, 0u, 0u, 0u};
+      }
     }
-    if constexpr (DT == DT_F32) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        q[g][w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, word(q[g], w)) * a.scale_log2);
-    }
-  }
+  };
   const float score_mul = DT == DT_F32 ? 1.0f : a.scale_log2;
-  const uint32_t lane_off = (uint32_t)rg * sg.tsb + (uint32_t)c * 16u;
+  const uint32_t tsb = (uint32_t)(a.st * EB);
+  const uint32_t lane_off = (uint32_t)rg * tsb + (uint32_t)c * 16u;
 
   float m[GC], l[GC], acc[GC][EPL];
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  }
-
-  const int nt = (int)((nkeys + TK - 1) / TK);
-
+  Segment sg;  // the current item's segment
   struct Tile {
     u4_t k[NI], v[NI];
   };
-  auto load_tile = [&](int j, Tile& t) {
+  auto load_tile_of = [&](const Segment& sgx, int j, Tile& t) {
     __amdgpu_buffer_rsrc_t rk, rv;
-    tile_rsrc<TK, D * EB>(sg, j, rk, rv);
+    tile_rsrc<TK, D * EB>(sgx, j, rk, rv);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) t.k[i] = buffer_load16(rk, lane_off + (uint32_t)(i * RPI) * sg.tsb);
+    for (int i = 0; i < NI; ++i) t.k[i] = buffer_load16(rk, lane_off + (uint32_t)(i * RPI) * tsb);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) t.v[i] = buffer_load16(rv, lane_off + (uint32_t)(i * RPI) * sg.tsb);
+    for (int i = 0; i < NI; ++i) t.v[i] = buffer_load16(rv, lane_off + (uint32_t)(i * RPI) * tsb);
   };
+  auto load_tile = [&](int j, Tile& t) { load_tile_of(sg, j, t); };
   auto compute_tile = [&](int j, const Tile& t) {
     const u4_t(&kt)[NI] = t.k;
     const u4_t(&vt)[NI] = t.v;
+    const int64_t nkeys = sg.nkeys;
     const int64_t k0 = (int64_t)j * TK;
     float s[NI][GC];
     bool valid[NI];
@@ -436,24 +511,37 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     }
   };
 
-  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, load_tile, compute_tile);
+  Tile buf[kPrefetchTiles + 1];
+  const WorkItem wi = decode_item<GC>(a, blockIdx.x);
+  load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
+  sg = locate_segment<EB>(a, wi, ls);
+  if (sg.b != wi.rank) load_q(wi, sg.b);
+  load_tile_of(sg, wave, buf[0]);
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        q[g][w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, word(q[g], w)) * a.scale_log2);
+  }
+#pragma unroll
+  for (int g = 0; g < GC; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+  }
+  const int nt = (int)((sg.nkeys + TK - 1) / TK);
+  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
   // ---- merge the lane groups of this wave (each has its own max) ----
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    float M = m[g];
-#pragma unroll
-    for (int mask = LPR; mask < kWave; mask <<= 1) M = fmaxf(M, __shfl_xor(M, mask));
+    const float M = across_groups<LPR>(m[g], OpMax{});
     const float f = m[g] == kNegInf ? 0.0f : fast_exp2(m[g] - M);
-    l[g] *= f;
+    l[g] = across_groups<LPR>(l[g] * f, OpAdd{});
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
-#pragma unroll
-    for (int mask = LPR; mask < kWave; mask <<= 1) {
-      l[g] += __shfl_xor(l[g], mask);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], mask);
-    }
+    for (int e = 0; e < EPL; ++e) acc[g][e] = across_groups<LPR>(acc[g][e] * f, OpAdd{});
     m[g] = M;
   }
 
@@ -531,48 +619,46 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
   const int R = lane >> 4;   // key group of this lane
   const int c = lane & 15;   // K row / query row / V chunk of this lane
 
-  const Segment sg = locate_segment<EB, GC>(a);
-  const int64_t nkeys = sg.nkeys;
-
-  // Q^T as the MFMA B operand: column c = query row h0 + c
+  const LaneSeqs ls = lane_seqs(a);
+  // Q^T as the MFMA B operand: column c = query row h0 + c of the current
+  // item (zero past the group)
   u4_t qb[KS];
+  auto load_q = [&](const WorkItem& w, int b) {
 #pragma unroll
-  for (int m = 0; m < KS; ++m) {
-    if (c < sg.nrows) {
-      const char* qp = static_cast<const char*>(a.q) +
-                       (((int64_t)sg.b * a.heads + sg.h0 + c) * D + 32 * m + 8 * R) * EB;
-      qb[m] = *reinterpret_cast<const u4_t*>(qp);
-    } else {
-      qb[m] = u4_t{0u, 0u, 0u, 0u};
+    for (int m = 0; m < KS; ++m) {
+      if (c < w.nrows) {
+        const char* qp = static_cast<const char*>(a.q) +
+                         (((int64_t)b * a.heads + w.h0 + c) * D + 32 * m + 8 * R) * EB;
+        qb[m] = *reinterpret_cast<const u4_t*>(qp);
+      } else {
+        qb[m] = u4_t{0u, 0u, 0u, 0u};
+      }
     }
-  }
-  const uint32_t k_off = (uint32_t)c * sg.tsb + (uint32_t)R * 16u;       // + 64*m
-  const uint32_t v_off = (uint32_t)(4 * R) * sg.tsb + (uint32_t)c * 16u;  // + i*tsb
+  };
+  const uint32_t tsb = (uint32_t)(a.st * EB);
+  const uint32_t k_off = (uint32_t)c * tsb + (uint32_t)R * 16u;       // + 64*m
+  const uint32_t v_off = (uint32_t)(4 * R) * tsb + (uint32_t)c * 16u;  // + i*tsb
 
-  float m_run = kNegInf, l_run = 0.0f;  // for (key group R, query row c)
+  float m_run, l_run;  // for (key group R, query row c)
   float acc[GC][8];
-#pragma unroll
-  for (int g = 0; g < GC; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
-
-  const int nt = (int)((nkeys + TK - 1) / TK);
-
+  Segment sg;  // the current item's segment
   struct Tile {
     u4_t k[KS], v[4];
   };
-  auto load_tile = [&](int j, Tile& t) {
+  auto load_tile_of = [&](const Segment& sgx, int j, Tile& t) {
     __amdgpu_buffer_rsrc_t rk, rv;
-    tile_rsrc<TK, D * EB>(sg, j, rk, rv);
+    tile_rsrc<TK, D * EB>(sgx, j, rk, rv);
 #pragma unroll
     for (int m = 0; m < KS; ++m) t.k[m] = buffer_load16(rk, k_off + 64u * m);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16(rv, v_off + (uint32_t)i * sg.tsb);
+    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16(rv, v_off + (uint32_t)i * tsb);
   };
+  auto load_tile = [&](int j, Tile& t) { load_tile_of(sg, j, t); };
 
   auto compute_tile = [&](int j, const Tile& t) {
     const u4_t(&kt)[KS] = t.k;
     const u4_t(&vt)[4] = t.v;
+    const int64_t nkeys = sg.nkeys;
     f4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < KS; ++m) s4 = mfma_qk<DT>(kt[m], qb[m], s4);
@@ -627,26 +713,30 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
     }
   };
 
-  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, load_tile, compute_tile);
+  Tile buf[kPrefetchTiles + 1];
+  const WorkItem wi = decode_item<GC>(a, blockIdx.x);
+  load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
+  sg = locate_segment<EB>(a, wi, ls);
+  if (sg.b != wi.rank) load_q(wi, sg.b);
+  load_tile_of(sg, wave, buf[0]);
+  m_run = kNegInf;
+  l_run = 0.0f;
+#pragma unroll
+  for (int g = 0; g < GC; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+  const int nt = (int)((sg.nkeys + TK - 1) / TK);
+  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
   // ---- merge the four key groups R of this wave ----
-  float M = m_run;
-  M = fmaxf(M, __shfl_xor(M, 16));
-  M = fmaxf(M, __shfl_xor(M, 32));
+  const float M = across_groups<16>(m_run, OpMax{});
   const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
-  float lw = l_run * f;
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
+  const float lw = across_groups<16>(l_run * f, OpAdd{});
   static_for<GC>([&](auto gi) {
     constexpr int g = decltype(gi)::value;
     const float fg = row_bcast<g>(f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = acc[g][e] * fg;
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[g][e] = x;
-    }
+    for (int e = 0; e < 8; ++e) acc[g][e] = across_groups<16>(acc[g][e] * fg, OpAdd{});
   });
 
   // ---- merge the waves through LDS and write the epilogue ----

@@ -178,11 +178,15 @@ int fd_decode_combine(const void* workspace, int batch, int heads, int dim,
  * QK^T and PV everywhere. FD_PATH_MFMA: QK^T on the matrix cores
  * (v_mfma_f32_16x16x32_{f16,bf16}) wherever that kernel exists -- fp16/bf16
  * at head dim 128 -- and the VALU kernel elsewhere. FD_PATH_AUTO (the
- * default): the library's measured choice. Both kernels compute the same
- * function to the same tolerances. Returns the previous setting, or -1
- * (setting unchanged) for an unknown value.
+ * default): the library's measured choice. FD_PATH_UNPACKED: the VALU
+ * kernel with one query head per workgroup, so each K/V row is read once
+ * per query head instead of once per GQA group -- the unpacked,
+ * FlashAttention-2-style decode that 04_flash_decoding.py (demos 2-3)
+ * compares flash decoding against; a comparator, never a default. All paths
+ * compute the same function to the same tolerances. Returns the previous
+ * setting, or -1 (setting unchanged) for an unknown value.
  */
-enum { FD_PATH_AUTO = 0, FD_PATH_VALU = 1, FD_PATH_MFMA = 2 };
+enum { FD_PATH_AUTO = 0, FD_PATH_VALU = 1, FD_PATH_MFMA = 2, FD_PATH_UNPACKED = 3 };
 int fd_set_kernel_path(int path);
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -192,7 +192,8 @@ def test_split_and_combine_reject_before_launch():
 def test_kernel_path_setting():
     prev = fd.fd_set_kernel_path(fd.FD_PATH_VALU)
     assert fd.fd_set_kernel_path(fd.FD_PATH_MFMA) == fd.FD_PATH_VALU
-    assert fd.fd_set_kernel_path(prev) == fd.FD_PATH_MFMA
+    assert fd.fd_set_kernel_path(fd.FD_PATH_UNPACKED) == fd.FD_PATH_MFMA
+    assert fd.fd_set_kernel_path(prev) == fd.FD_PATH_UNPACKED
     assert _lib().fd_set_kernel_path(7) == -1
     with pytest.raises(ValueError):
         fd.fd_set_kernel_path(9)

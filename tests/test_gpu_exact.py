@@ -23,12 +23,14 @@ def _gpu():
     H.fd().fd_set_kernel_path(H.fd().FD_PATH_AUTO)
 
 
-@pytest.fixture(params=["valu", "mfma"])
+@pytest.fixture(params=["valu", "mfma", "unpacked"])
 def kernel_path(request):
     """Run the test on each split kernel (MFMA falls back to VALU where the
-    matrix-core kernel does not exist)."""
+    matrix-core kernel does not exist; "unpacked" is the VALU kernel with one
+    query head per workgroup)."""
     fd = H.fd()
-    prev = fd.fd_set_kernel_path({"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA}[request.param])
+    prev = fd.fd_set_kernel_path({"valu": fd.FD_PATH_VALU, "mfma": fd.FD_PATH_MFMA,
+                                  "unpacked": fd.FD_PATH_UNPACKED}[request.param])
     H.announce("kernel path", request.param)
     yield request.param
     fd.fd_set_kernel_path(prev)

@@ -69,6 +69,21 @@ def test_fd_microbenchmark_shapes(batch, kv_len):
     check_full(inp, ns)
 
 
+@pytest.mark.parametrize("batch,kv_len", W.FD_UBENCH_SHAPES)
+def test_unpacked_comparator_shapes(batch, kv_len):
+    """The unpacked comparison path (one query head per workgroup, no split,
+    as in 04_flash_decoding.py demos 2-3) on the same shapes gives the
+    oracle's result."""
+    w = W.fd_ubench(batch, kv_len)
+    inp = W.make_inputs(w, H.DEV)
+    fd = H.fd()
+    prev = fd.fd_set_kernel_path(fd.FD_PATH_UNPACKED)
+    try:
+        check_full(inp, 1)
+    finally:
+        fd.fd_set_kernel_path(prev)
+
+
 @pytest.mark.parametrize("kv_len", W.LLAMA_LENS)
 @pytest.mark.parametrize("batch", W.LLAMA_BATCHES)
 def test_llama_long_context(batch, kv_len):

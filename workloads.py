@@ -92,6 +92,10 @@ def fd_ubench(batch: int, kv_len: int) -> Workload:
                     kv_len=kv_len, notes="flash-decoding blog shape, 04_flash_decoding.py demo 3")
 
 
+# 04_flash_decoding.py demo 4: the split-count sweep at 16/2 heads
+DEMO4_SHAPES = [(1, 65536), (8, 8192), (64, 2048)]
+DEMO4_SPLITS = [1, 2, 4, 8, 16, 32, 64, 128]
+
 LLAMA_LENS = [1024, 8192, 32768, 131072]
 LLAMA_BATCHES = [1, 16]
 LLAMA_SWEEP_SPLITS = [1, 2, 4, 8, 16, 32, 64, 128]
@@ -113,6 +117,7 @@ def varlen_qwen() -> Workload:
 def all_workloads() -> list[Workload]:
     out = [tiny()] + [mha(d) for d in (16, 32, 64, 128)]
     out += [fd_ubench(b, s) for b, s in FD_UBENCH_SHAPES]
+    out += [fd_ubench(b, s) for b, s in DEMO4_SHAPES if (b, s) not in FD_UBENCH_SHAPES]
     out += [llama(b, s) for s in LLAMA_LENS for b in LLAMA_BATCHES]
     out += [llama(1, 65536, ns) for ns in LLAMA_SWEEP_SPLITS]
     out.append(varlen_qwen())
