@@ -31,6 +31,17 @@ design notes):
   * ``scale`` multiplies q.k before the softmax (natural-exp units).
   * A split with no keys is an error (the page says the scheduler must
     prevent it), so ``split_bounds`` raises when num_splits > seqlen.
+
+The second split format, that of ``_splitk_stage1_kernel`` /
+``_splitk_reduce_kernel`` in "flash_decode_splitk.py" (MiniInfer), is here
+too: ceil-equal split bounds (``split_bounds_ceil``, empty tail splits
+allowed) and the unnormalised per-split state (running max m, sum l and
+accumulator acc in base-2 units of the scaled scores, ``split_states_rows``)
+merged by rescaling to the largest m (``merge_states``). Readings: a split
+with no keys has state (-inf, 0, 0) (the stage-1 kernel's initial values,
+written unchanged when its key loop is empty); a row whose splits are all
+empty merges to zeros (the page's host check keeps KV_LEN >= 1, so it
+never reaches that case).
 """
 from __future__ import annotations
 
@@ -49,6 +60,11 @@ __all__ = [
     "attention_split_merge",
     "head_pairs",
     "default_scale",
+    "split_bounds_ceil",
+    "split_states_rows",
+    "merge_states",
+    "attention_states",
+    "attention_split_merge_states",
 ]
 
 
@@ -241,3 +257,117 @@ def attention_split_merge(q, k, v, cu_seqlens_k, heads: int, kv_heads: int,
 def default_scale(dim: int) -> float:
     """1/sqrt(dim), the default of flash_decode_splitk.py."""
     return 1.0 / math.sqrt(dim)
+
+
+# --------------------------------------------------------------------------
+# MiniInfer's format: ceil-equal bounds, unnormalised (m, l, acc) state
+# --------------------------------------------------------------------------
+LOG2E = 1.0 / math.log(2.0)
+
+
+def split_bounds_ceil(seqlen: int, num_splits: int) -> list[tuple[int, int]]:
+    """Ceil-equal split bounds of one sequence.
+
+    flash_decode_splitk.py, ``_splitk_stage1_kernel``: every split spans
+    ``size = ceil(seqlen / num_splits)`` keys from ``sid * size``, cut at
+    ``seqlen``. Splits that start at or past the end are empty; they are
+    returned as ``(seqlen, seqlen)``. num_splits < 1 raises.
+    """
+    seqlen = int(seqlen)
+    num_splits = int(num_splits)
+    if num_splits < 1:
+        raise ValueError("num_splits must be >= 1")
+    if seqlen < 0:
+        raise ValueError("seqlen must be >= 0")
+    size = -(-seqlen // num_splits)
+    return [(min(s * size, seqlen), min(s * size + size, seqlen)) for s in range(num_splits)]
+
+
+def split_states_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                      num_splits: int, scale: float):
+    """Unnormalised state of every ceil-equal split of one KV sequence.
+
+    With base-2 scaled scores s2_t = scale * log2(e) * q.k_t
+    (``q * (sm_scale * 1.44269504)`` in _splitk_stage1_kernel), over the keys
+    t of split s:  m_s = max_t s2_t,  l_s = sum_t 2^(s2_t - m_s),
+    acc_s = sum_t 2^(s2_t - m_s) v_t  -- the values the stage-1 kernel's
+    running update ends with. An empty split has (-inf, 0, 0).
+    Returns (m [ns, R], l [ns, R], acc [R, ns, D]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    R, D = q.shape
+    m = np.full((num_splits, R), -np.inf, dtype=np.float64)
+    l = np.zeros((num_splits, R), dtype=np.float64)
+    acc = np.zeros((R, num_splits, D), dtype=np.float64)
+    for s_idx, (a, e) in enumerate(split_bounds_ceil(k.shape[0], num_splits)):
+        if e <= a:
+            continue
+        s2 = (scale * LOG2E) * (q @ k[a:e].T)   # [R, e-a]
+        ms = s2.max(axis=1)
+        p = np.exp2(s2 - ms[:, None])
+        m[s_idx] = ms
+        l[s_idx] = p.sum(axis=1)
+        acc[:, s_idx, :] = p @ v[a:e]
+    return m, l, acc
+
+
+def merge_states(m: np.ndarray, l: np.ndarray, acc: np.ndarray) -> np.ndarray:
+    """_splitk_reduce_kernel for one set of rows: m, l [ns, R], acc [R, ns, D]
+    -> o [R, D] with M = max_s m_s, alpha_s = 2^(m_s - M),
+    o = sum_s alpha_s acc_s / sum_s alpha_s l_s. Rows whose splits are all
+    empty (M = -inf) give zeros."""
+    m = np.asarray(m, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    acc = np.asarray(acc, dtype=np.float64)
+    R = m.shape[1]
+    out = np.zeros((R, acc.shape[2]), dtype=np.float64)
+    for r in range(R):
+        M = m[:, r].max()
+        if M == -np.inf:
+            continue
+        alpha = np.exp2(m[:, r] - M)            # 0 for empty splits
+        out[r] = (alpha @ acc[r]) / (alpha @ l[:, r])
+    return out
+
+
+def attention_states(q, k, v, cu_seqlens_k, heads: int, kv_heads: int,
+                     num_splits: int, scale: float, layout: str = "packed", pairs=None):
+    """Stage 1 for a whole batch: (m [batch, heads, ns], l [batch, heads, ns],
+    acc [batch, heads, ns, dim]), the shapes of M_BUF / L_BUF ([bh, ns]) and
+    ACC_BUF ([bh, ns, dim]) in flash_decode_splitk.py. Pairs not in ``pairs``
+    are NaN."""
+    _check(q, cu_seqlens_k, heads, kv_heads)
+    B, H, D = q.shape
+    m = np.full((B, H, num_splits), np.nan, dtype=np.float64)
+    l = np.full((B, H, num_splits), np.nan, dtype=np.float64)
+    acc = np.full((B, H, num_splits, D), np.nan, dtype=np.float64)
+    groups = dict(head_pairs(heads, kv_heads))
+    todo = pairs if pairs is not None else [(b, j) for b in range(B) for j in range(kv_heads)]
+    for b, j in todo:
+        hs = groups[j]
+        kr = kv_rows(k, cu_seqlens_k, b, j, layout)
+        vr = kv_rows(v, cu_seqlens_k, b, j, layout)
+        ms, ls, accs = split_states_rows(np.asarray(q[b, hs, :], dtype=np.float64), kr, vr,
+                                         num_splits, scale)
+        m[b, hs, :] = ms.T
+        l[b, hs, :] = ls.T
+        acc[b, hs, :, :] = accs
+    return m, l, acc
+
+
+def attention_split_merge_states(q, k, v, cu_seqlens_k, heads: int, kv_heads: int,
+                                 num_splits: int, scale: float, layout: str = "packed",
+                                 pairs=None) -> np.ndarray:
+    """Stage 1 then the reduce, for a whole batch: o [batch, heads, dim]."""
+    m, l, acc = attention_states(q, k, v, cu_seqlens_k, heads, kv_heads, num_splits, scale,
+                                 layout, pairs)
+    B, H, ns, D = acc.shape
+    out = np.full((B, H, D), np.nan, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            if np.isnan(m[b, h, 0]):
+                continue
+            out[b, h:h + 1, :] = merge_states(m[b, h][:, None], l[b, h][:, None], acc[b, h:h + 1])
+    return out

@@ -285,5 +285,145 @@ def pin_metamorphic(orc):
     assert np.abs((l2 - l1) - 1.5).max() < 1e-13
 
 
+# --------------------------------------------------------------------------
+# MiniInfer's format: ceil-equal bounds and unnormalised (m, l, acc) states
+# --------------------------------------------------------------------------
+def pin_split_bounds_ceil(orc, max_len: int = 120):
+    """Ceil-equal bounds (flash_decode_splitk.py, stage-1 kernel), for every
+    0 <= L <= max_len and 1 <= ns <= 2L + 2: the non-empty splits come first
+    and tile [0, L) in order; all of them but the last have the same size,
+    the last at most that size and at least 1 key; that common size is the
+    smallest with which ns splits reach L; every later split is (L, L).
+    Worked example: L = 10, ns = 6 gives five splits of 2 keys and an empty
+    sixth. ns < 1 raises."""
+    for L in range(0, max_len + 1):
+        for ns in range(1, 2 * L + 3):
+            b = orc.split_bounds_ceil(L, ns)
+            assert len(b) == ns, (L, ns)
+            nonempty = [x for x in b if x[1] > x[0]]
+            n = len(nonempty)
+            assert b[:n] == nonempty, (L, ns, b)
+            assert all(x == (L, L) for x in b[n:]), (L, ns, b)
+            pos = 0
+            for a, e in nonempty:
+                assert a == pos, (L, ns, b)
+                pos = e
+            assert pos == L, (L, ns, b)
+            if n:
+                size = nonempty[0][1] - nonempty[0][0]
+                assert all(e - a == size for a, e in nonempty[:-1]), (L, ns, b)
+                assert 1 <= nonempty[-1][1] - nonempty[-1][0] <= size
+                # the smallest size with which ns equal splits cover L
+                assert size * ns >= L and (size - 1) * ns < L, (L, ns, size)
+    assert orc.split_bounds_ceil(10, 6) == [(0, 2), (2, 4), (4, 6), (6, 8), (8, 10), (10, 10)]
+    for bad in (0, -3):
+        try:
+            orc.split_bounds_ceil(10, bad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("num_splits < 1 must raise")
+
+
+def _decimal_states(q, k, v, scale):
+    """m = max_t s2_t, l = sum_t 2^(s2_t - m), acc = sum_t 2^(s2_t - m) v_t at
+    50 digits, s2_t = scale * q.k_t / ln 2."""
+    getcontext().prec = 50
+    ln2 = Decimal(2).ln()
+    R, D = q.shape
+    L = k.shape[0]
+    sc = Decimal(repr(float(scale)))
+    ms, ls, accs = [], [], []
+    for r in range(R):
+        s2 = [sc * sum(Decimal(repr(float(q[r, d]))) * Decimal(repr(float(k[t, d])))
+                       for d in range(D)) / ln2 for t in range(L)]
+        m = max(s2)
+        w = [((x - m) * ln2).exp() for x in s2]
+        ms.append(float(m))
+        ls.append(float(sum(w)))
+        accs.append([float(sum(w[t] * Decimal(repr(float(v[t, d]))) for t in range(L)))
+                     for d in range(D)])
+    return np.array(ms), np.array(ls), np.array(accs)
+
+
+def pin_states_decimal(orc):
+    """Per-split states against a 50-digit brute force on tiny inputs, for
+    every split count up to L + 3 (empty tail splits included), and their
+    merge against the brute-force direct attention."""
+    rng = _rng(5)
+    for trial in range(5):
+        R = int(rng.integers(1, 4))
+        L = int(rng.integers(1, 11))
+        D = int(rng.integers(1, 5))
+        q = rng.standard_normal((R, D)) * 2
+        k = rng.standard_normal((L, D)) * 2
+        v = rng.standard_normal((L, D))
+        scale = float(rng.uniform(0.2, 1.5))
+        ref_o, _ = _decimal_attention(q, k, v, scale)
+        for ns in range(1, L + 4):
+            m, l, acc = orc.split_states_rows(q, k, v, ns, scale)
+            assert m.shape == (ns, R) and l.shape == (ns, R) and acc.shape == (R, ns, D)
+            for s, (a, e) in enumerate(orc.split_bounds_ceil(L, ns)):
+                if e == a:
+                    assert np.all(m[s] == -np.inf) and not l[s].any() and not acc[:, s].any()
+                    continue
+                dm, dl, dacc = _decimal_states(q, k[a:e], v[a:e], scale)
+                assert np.abs(m[s] - dm).max() < 1e-13, ("m", trial, ns, s)
+                assert np.abs(l[s] - dl).max() < 1e-13 * max(1.0, dl.max()), ("l", trial, ns, s)
+                assert np.abs(acc[:, s] - dacc).max() < 1e-13 * max(1.0, np.abs(dacc).max())
+            o = orc.merge_states(m, l, acc)
+            assert np.abs(o - ref_o).max() < 1e-13, ("merge", trial, ns)
+
+
+def pin_states_closed_forms(orc):
+    rng = _rng(6)
+    D, L = 16, 37
+    k = rng.standard_normal((L, D))
+    v = rng.standard_normal((L, D))
+    # zero query: every s2 is 0, so m_s = 0, l_s = key count, acc_s = sum of V
+    m, l, acc = orc.split_states_rows(np.zeros((2, D)), k, v, 5, 0.3)
+    for s, (a, e) in enumerate(orc.split_bounds_ceil(L, 5)):
+        assert np.all(m[s] == 0.0) and np.all(l[s] == e - a)
+        assert np.abs(acc[:, s] - v[a:e].sum(axis=0)).max() < 1e-13
+    # one key per split: l = 1, acc = v, m = scale * q.k / ln 2
+    q = rng.standard_normal((3, D))
+    m, l, acc = orc.split_states_rows(q, k[:4], v[:4], 4, 0.7)
+    assert np.all(l == 1.0) and np.array_equal(acc, np.broadcast_to(v[:4], (3, 4, D)))
+    assert np.abs(m - 0.7 * (q @ k[:4].T).T / math.log(2.0)).max() < 1e-13
+    # the merge does not depend on each split's reference max: (m + c,
+    # l * 2^-c, acc * 2^-c) merges to the same output
+    m, l, acc = orc.split_states_rows(q, k, v, 6, 0.4)
+    c = rng.uniform(-3, 3, size=(6, 1))
+    o1 = orc.merge_states(m, l, acc)
+    o2 = orc.merge_states(m + c, l * np.exp2(-c), acc * np.exp2(-c).T[:, :, None])
+    assert np.abs(o1 - o2).max() < 1e-13
+    # a row whose splits are all empty merges to zeros
+    z = orc.merge_states(np.full((3, 2), -np.inf), np.zeros((3, 2)), np.zeros((2, 3, D)))
+    assert not z.any()
+
+
+def pin_states_sdpa(orc):
+    """Stage 1 + reduce for whole batches against torch float64 SDPA, both
+    layouts, GQA, split counts beyond the sequence length (empty splits)."""
+    rng = _rng(7)
+    for (B, H, Hkv, D, L, ns) in [(2, 4, 4, 64, 256, 4), (1, 8, 1, 128, 300, 7),
+                                  (3, 28, 4, 32, 10, 6), (2, 32, 8, 16, 5, 16)]:
+        q = rng.standard_normal((B, H, D))
+        kb = rng.standard_normal((B, Hkv, L, D))
+        vb = rng.standard_normal((B, Hkv, L, D))
+        cu = [b * L for b in range(B + 1)]
+        scale = 1.0 / math.sqrt(D)
+        ref = _sdpa(q, kb, vb, scale, H // Hkv)
+        o = orc.attention_split_merge_states(q, kb, vb, cu, H, Hkv, ns, scale, layout="bhsd")
+        assert np.abs(o - ref).max() < 1e-12, ("bhsd", B, H, Hkv, D, ns)
+        kp = kb.transpose(0, 2, 1, 3).reshape(B * L, Hkv, D)
+        vp = vb.transpose(0, 2, 1, 3).reshape(B * L, Hkv, D)
+        o = orc.attention_split_merge_states(q, kp, vp, cu, H, Hkv, ns, scale, layout="packed")
+        assert np.abs(o - ref).max() < 1e-12, ("packed", B, H, Hkv, D, ns)
+        m, l, acc = orc.attention_states(q, kp, vp, cu, H, Hkv, ns, scale)
+        assert m.shape == (B, H, ns) and l.shape == (B, H, ns) and acc.shape == (B, H, ns, D)
+
+
 ALL_PINS = [pin_split_bounds, pin_closed_forms, pin_decimal_bruteforce, pin_torch_sdpa,
-            pin_split_invariant, pin_metamorphic]
+            pin_split_invariant, pin_metamorphic, pin_split_bounds_ceil, pin_states_decimal,
+            pin_states_closed_forms, pin_states_sdpa]

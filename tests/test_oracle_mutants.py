@@ -14,7 +14,9 @@ import oracle.attention as A
 from tests import oracle_pins as pins
 
 _orig = {n: getattr(A, n) for n in ("split_bounds", "kv_rows", "attention_rows",
-                                     "split_partials_rows", "merge_partials", "head_pairs")}
+                                     "split_partials_rows", "merge_partials", "head_pairs",
+                                     "split_bounds_ceil", "split_states_rows",
+                                     "merge_states")}
 
 
 def _bounds_ceil_equal(seqlen, num_splits):
@@ -99,7 +101,80 @@ def _merge_weight_by_dim(o_parts, lse):
     return np.einsum("sr,rsd->rd", w, np.asarray(o_parts, dtype=np.float64))
 
 
+def _ceil_bounds_floor_size(seqlen, num_splits):
+    # size = floor(L/ns) with the remainder dropped
+    if num_splits < 1:
+        raise ValueError
+    size = seqlen // num_splits
+    return [(min(s * size, seqlen), min(s * size + size, seqlen)) for s in range(num_splits)]
+
+
+def _ceil_bounds_proportional(seqlen, num_splits):
+    # the proportional rule where the ceil-equal one is meant
+    if num_splits < 1:
+        raise ValueError
+    return [(seqlen * s // num_splits, seqlen * (s + 1) // num_splits) for s in range(num_splits)]
+
+
+def _states_natural_exp(q, k, v, ns, scale):
+    # weights e^(s2 - m) instead of 2^(s2 - m)
+    m, l, acc = _orig["split_states_rows"](q, k, v, ns, scale)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    for s, (a, e) in enumerate(A.split_bounds_ceil(k.shape[0], ns)):
+        if e > a:
+            s2 = scale / np.log(2.0) * (q @ k[a:e].T)
+            p = np.exp(s2 - s2.max(axis=1, keepdims=True))
+            l[s] = p.sum(axis=1)
+            acc[:, s, :] = p @ v[a:e]
+    return m, l, acc
+
+
+def _states_normalised(q, k, v, ns, scale):
+    # acc divided by l already (the other format's o_s)
+    m, l, acc = _orig["split_states_rows"](q, k, v, ns, scale)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        acc = np.where(l.T[:, :, None] > 0, acc / l.T[:, :, None], 0.0)
+    return m, l, acc
+
+
+def _states_natural_max(q, k, v, ns, scale):
+    # m kept in natural-log units while the weights use base 2
+    m, l, acc = _orig["split_states_rows"](q, k, v, ns, scale)
+    return m * np.log(2.0), l, acc
+
+
+def _merge_states_no_alpha_on_l(m, l, acc):
+    m = np.asarray(m); l = np.asarray(l); acc = np.asarray(acc)
+    out = np.zeros((m.shape[1], acc.shape[2]))
+    for r in range(m.shape[1]):
+        M = m[:, r].max()
+        if M == -np.inf:
+            continue
+        alpha = np.exp2(m[:, r] - M)
+        out[r] = (alpha @ acc[r]) / l[:, r].sum()
+    return out
+
+
+def _merge_states_sum_acc(m, l, acc):
+    m = np.asarray(m); l = np.asarray(l); acc = np.asarray(acc)
+    out = np.zeros((m.shape[1], acc.shape[2]))
+    for r in range(m.shape[1]):
+        if m[:, r].max() == -np.inf:
+            continue
+        out[r] = acc[r].sum(axis=0) / l[:, r].sum()
+    return out
+
+
 MUTANTS = {
+    "ceil_bounds_floor_size": ("split_bounds_ceil", _ceil_bounds_floor_size),
+    "ceil_bounds_proportional": ("split_bounds_ceil", _ceil_bounds_proportional),
+    "states_natural_exp": ("split_states_rows", _states_natural_exp),
+    "states_normalised": ("split_states_rows", _states_normalised),
+    "states_natural_max": ("split_states_rows", _states_natural_max),
+    "merge_states_no_alpha_on_l": ("merge_states", _merge_states_no_alpha_on_l),
+    "merge_states_sum_acc": ("merge_states", _merge_states_sum_acc),
     "bounds_ceil_equal": ("split_bounds", _bounds_ceil_equal),
     "bounds_off_by_one": ("split_bounds", _bounds_off_by_one),
     "heads_modulo": ("head_pairs", _heads_modulo),
@@ -116,7 +191,9 @@ MUTANTS = {
 
 # cheapest pins first; the test stops at the first one that rejects the mutant
 _ORDER = [pins.pin_closed_forms, pins.pin_metamorphic, pins.pin_split_bounds,
-          pins.pin_torch_sdpa, pins.pin_decimal_bruteforce, pins.pin_split_invariant]
+          pins.pin_split_bounds_ceil, pins.pin_states_closed_forms, pins.pin_torch_sdpa,
+          pins.pin_states_sdpa, pins.pin_decimal_bruteforce, pins.pin_states_decimal,
+          pins.pin_split_invariant]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
