@@ -79,7 +79,7 @@ def traffic_for(workload_name: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, ns, budget_s: float):
+def cpu_baseline(inp, ns, budget_s: float, fmt: str = "lse"):
     """The fp64 numpy oracle (split + merge) on the same workload, one
     (sequence, KV head) unit at a time in order, repeated until its own
     compute time reaches ~budget_s seconds; BLAS limited to one thread.
@@ -106,7 +106,11 @@ def cpu_baseline(inp, ns, budget_s: float):
                 kr = inp.k[b, j, :L].float().cpu().numpy()
                 vr = inp.v[b, j, :L].float().cpu().numpy()
             t1 = time.perf_counter()
-            if L > 0:
+            if L > 0 and fmt == "unnorm":
+                m, l, acc = oracle.split_states_rows(q[b, j * G:(j + 1) * G], kr, vr, ns,
+                                                     w.sm_scale)
+                oracle.merge_states(m, l, acc)
+            elif L > 0:
                 op, lse = oracle.split_partials_rows(q[b, j * G:(j + 1) * G], kr, vr,
                                                      min(ns, L), w.sm_scale)
                 oracle.merge_partials(op, lse)
@@ -131,7 +135,7 @@ def split_workgroups(w, ns: int, rows_per_workgroup: int) -> int:
 
 
 def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES,
-        ns_override: int = 0, rows_per_workgroup: int = 8):
+        ns_override: int = 0, rows_per_workgroup: int = 8, fmt: str = "lse"):
     import torch
     import workloads as W
     import decode_attention_09_amd as fd
@@ -146,19 +150,22 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     vs = [inp.v] + [inp.v.clone() for _ in range(copies - 1)]
     out = torch.empty_like(inp.q)
     B, Hq, D = w.batch, w.heads, w.dim
-    ws = torch.empty(max(1, fd.fd_workspace_bytes(B, Hq, D, ns)), dtype=torch.uint8, device=dev)
+    unnorm = fmt == "unnorm"
+    ws_bytes = (fd.fd_workspace_bytes_unnorm if unnorm else fd.fd_workspace_bytes)(B, Hq, D, ns)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     single_launch = ns == 1
+    attention = fd.fd_decode_attention_unnorm if unnorm else fd.fd_decode_attention
+    split = fd.fd_decode_split_unnorm if unnorm else fd.fd_decode_split
 
     def step(i):
         k, v = ks[i % copies], vs[i % copies]
-        fd.fd_decode_attention(inp.q, k, v, inp.cu_seqlens_k, ns, out=out, workspace=ws,
-                               layout=w.layout, stream=stream)
+        attention(inp.q, k, v, inp.cu_seqlens_k, ns, out=out, workspace=ws, layout=w.layout,
+                  stream=stream)
 
     def split_only(i):
         k, v = ks[i % copies], vs[i % copies]
-        fd.fd_decode_split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
-                           stream=stream)
+        split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout, stream=stream)
 
     def timed(fn, n, offset):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -199,6 +206,8 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
                    "kv_heads": w.kv_heads, "head_dim": w.dim, "kv_len_total": sum(inp.lengths),
                    "layout": w.layout, "num_splits": ns,
+                   "partials": "(m, l, acc), ceil-equal bounds" if unnorm
+                   else "(o_s, lse_s), proportional bounds",
                    "split_workgroups": split_workgroups(w, ns, rows_per_workgroup),
                    "kv_bytes": kv_bytes,
                    "kv_copies_rotated": copies, "parallelism": "single GPU"},
@@ -211,7 +220,7 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
         "wall_s_timed": round(wall, 4),
     }
     if cpu_s > 0:
-        res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s)
+        res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s, fmt)
     return res
 
 
@@ -242,6 +251,9 @@ def main():
                     default="auto",
                     help="split kernel variant (default: the library's own choice; "
                          "unpacked = one query head per workgroup, the comparison path)")
+    ap.add_argument("--format", choices=["lse", "unnorm"], default="lse",
+                    help="split format: normalised partials + LSE with proportional bounds "
+                         "(default), or (m, l, acc) with ceil-equal bounds")
     ap.add_argument("--sweep-splits", default="",
                     help="comma-separated split counts: one line (no CPU leg) per "
                          "workload in --workload (comma-separated) and split count")
@@ -271,13 +283,14 @@ def main():
             todo = [(workload_by_name(n), ns) for n in args.workload.split(",")
                     for ns in splits]
         for w, ns in todo:
-            r = run(w, args.steps, args.warmup, 0.0, ns_override=ns, rows_per_workgroup=rows)
+            r = run(w, args.steps, args.warmup, 0.0, ns_override=ns, rows_per_workgroup=rows,
+                    fmt=args.format)
             r["kernel_path"] = args.kernel_path
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
         return
     r = run(workload_by_name(args.workload), args.steps, args.warmup, args.cpu_seconds,
-            ns_override=args.num_splits, rows_per_workgroup=rows)
+            ns_override=args.num_splits, rows_per_workgroup=rows, fmt=args.format)
     r["kernel_path"] = args.kernel_path
     print(json.dumps(r), flush=True)
 

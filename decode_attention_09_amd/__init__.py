@@ -17,6 +17,8 @@ __all__ = [
     "fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
     "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path", "kv_layout",
     "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "FD_PATH_UNPACKED", "workspace_views",
+    "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
+    "fd_decode_attention_unnorm", "workspace_views_unnorm",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
@@ -76,6 +78,14 @@ def load_library():
     lib.fd_decode_split.restype = i32
     lib.fd_decode_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32]
     lib.fd_decode_combine.restype = i32
+    lib.fd_workspace_bytes_unnorm.argtypes = [i32, i32, i32, i32]
+    lib.fd_workspace_bytes_unnorm.restype = ctypes.c_size_t
+    lib.fd_decode_attention_unnorm.argtypes = lib.fd_decode_attention.argtypes
+    lib.fd_decode_attention_unnorm.restype = i32
+    lib.fd_decode_split_unnorm.argtypes = lib.fd_decode_split.argtypes
+    lib.fd_decode_split_unnorm.restype = i32
+    lib.fd_decode_combine_unnorm.argtypes = lib.fd_decode_combine.argtypes
+    lib.fd_decode_combine_unnorm.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -162,6 +172,10 @@ def fd_workspace_bytes(batch: int, heads: int, dim: int, num_splits: int) -> int
     return int(load_library().fd_workspace_bytes(batch, heads, dim, num_splits))
 
 
+def fd_workspace_bytes_unnorm(batch: int, heads: int, dim: int, num_splits: int) -> int:
+    return int(load_library().fd_workspace_bytes_unnorm(batch, heads, dim, num_splits))
+
+
 def _sizes(q, k, cu):
     if q.dim() != 3:
         raise ValueError("q must be [batch, heads, dim]")
@@ -174,9 +188,10 @@ def _sizes(q, k, cu):
     return batch, heads, kv_heads, dim
 
 
-def _workspace(q, batch, heads, dim, num_splits, workspace):
+def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
     import torch
-    need = fd_workspace_bytes(batch, heads, dim, num_splits)
+    size = fd_workspace_bytes_unnorm if unnorm else fd_workspace_bytes
+    need = size(batch, heads, dim, num_splits)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
@@ -184,9 +199,8 @@ def _workspace(q, batch, heads, dim, num_splits, workspace):
     return workspace
 
 
-def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
-                        out=None, workspace=None, layout: str = "packed", stream=None):
-    """out[b,h] = softmax(scale q[b,h].K_b^T) V_b through libfd's two launches."""
+def _attention(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, out, workspace, layout,
+               stream):
     import torch
     batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
     if scale is None:
@@ -194,48 +208,104 @@ def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int, scale: float | N
     if out is None:
         out = torch.empty_like(q)
     if num_splits > 1:
-        workspace = _workspace(q, batch, heads, dim, num_splits, workspace)
+        workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
     lay = kv_layout(k, layout)
-    _check(load_library().fd_decode_attention(
+    _check(getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
         int(num_splits), float(scale), _ptr(out), _ptr(workspace), _stream(stream, q.device),
-        _dtype_code(q), ctypes.byref(lay)), "fd_decode_attention")
+        _dtype_code(q), ctypes.byref(lay)), name)
     return out
+
+
+def _split(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, workspace, layout, stream):
+    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
+    lay = kv_layout(k, layout)
+    _check(getattr(load_library(), name)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
+        int(num_splits), float(scale), _ptr(workspace), _stream(stream, q.device),
+        _dtype_code(q), ctypes.byref(lay)), name)
+    return workspace
+
+
+def _combine(name, workspace, batch, heads, dim, num_splits, out, stream):
+    _check(getattr(load_library(), name)(
+        _ptr(workspace), batch, heads, dim, int(num_splits), _ptr(out),
+        _stream(stream, out.device), _dtype_code(out)), name)
+    return out
+
+
+def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
+                        out=None, workspace=None, layout: str = "packed", stream=None):
+    """out[b,h] = softmax(scale q[b,h].K_b^T) V_b through libfd's two launches."""
+    return _attention("fd_decode_attention", False, q, k, v, cu_seqlens_k, num_splits, scale,
+                      out, workspace, layout, stream)
 
 
 def fd_decode_split(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
                     workspace=None, layout: str = "packed", stream=None):
     """First launch only; returns the workspace (uint8 tensor)."""
-    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
-    if scale is None:
-        scale = 1.0 / math.sqrt(dim)
-    workspace = _workspace(q, batch, heads, dim, num_splits, workspace)
-    lay = kv_layout(k, layout)
-    _check(load_library().fd_decode_split(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
-        int(num_splits), float(scale), _ptr(workspace), _stream(stream, q.device),
-        _dtype_code(q), ctypes.byref(lay)), "fd_decode_split")
-    return workspace
+    return _split("fd_decode_split", False, q, k, v, cu_seqlens_k, num_splits, scale,
+                  workspace, layout, stream)
 
 
 def fd_decode_combine(workspace, batch: int, heads: int, dim: int, num_splits: int, out,
                       stream=None):
     """Second launch only: merge the workspace into out [batch, heads, dim]."""
-    _check(load_library().fd_decode_combine(
-        _ptr(workspace), batch, heads, dim, int(num_splits), _ptr(out),
-        _stream(stream, out.device), _dtype_code(out)), "fd_decode_combine")
-    return out
+    return _combine("fd_decode_combine", workspace, batch, heads, dim, num_splits, out, stream)
+
+
+def fd_decode_attention_unnorm(q, k, v, cu_seqlens_k, num_splits: int,
+                               scale: float | None = None, out=None, workspace=None,
+                               layout: str = "packed", stream=None):
+    """The same attention with ceil-equal bounds and (m, l, acc) partials."""
+    return _attention("fd_decode_attention_unnorm", True, q, k, v, cu_seqlens_k, num_splits,
+                      scale, out, workspace, layout, stream)
+
+
+def fd_decode_split_unnorm(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
+                           workspace=None, layout: str = "packed", stream=None):
+    """Split launch of the (m, l, acc) format; returns the workspace."""
+    return _split("fd_decode_split_unnorm", True, q, k, v, cu_seqlens_k, num_splits, scale,
+                  workspace, layout, stream)
+
+
+def fd_decode_combine_unnorm(workspace, batch: int, heads: int, dim: int, num_splits: int, out,
+                             stream=None):
+    """Combine launch of the (m, l, acc) format."""
+    return _combine("fd_decode_combine_unnorm", workspace, batch, heads, dim, num_splits, out,
+                    stream)
+
+
+def _f32_view(flat, off, shape):
+    import torch
+    n = 1
+    for x in shape:
+        n *= x
+    return flat[off:off + n * 4].view(torch.float32).view(*shape)
 
 
 def workspace_views(workspace, batch: int, heads: int, dim: int, num_splits: int):
     """(Opart [B,H,ns,D], LSE [B,ns,H]) fp32 views of a workspace, per the
     layout documented in include/fd.h."""
     import torch
+    flat = workspace.view(torch.uint8)
     n_o = batch * heads * num_splits * dim
     off = ((n_o * 4 + 255) // 256) * 256
-    flat = workspace.view(torch.uint8)
-    opart = flat[:n_o * 4].view(torch.float32).view(batch, heads, num_splits, dim)
-    lse = flat[off:off + batch * num_splits * heads * 4].view(torch.float32).view(
-        batch, num_splits, heads)
-    return opart, lse
+    return (_f32_view(flat, 0, (batch, heads, num_splits, dim)),
+            _f32_view(flat, off, (batch, num_splits, heads)))
 
+
+def workspace_views_unnorm(workspace, batch: int, heads: int, dim: int, num_splits: int):
+    """(ACC [B,H,ns,D], M [B,H,ns], L [B,H,ns]) fp32 views of an
+    unnormalised-format workspace, per the layout documented in include/fd.h."""
+    import torch
+    flat = workspace.view(torch.uint8)
+    rows = batch * heads * num_splits
+    off_m = ((rows * dim * 4 + 255) // 256) * 256
+    off_l = off_m + ((rows * 4 + 255) // 256) * 256
+    return (_f32_view(flat, 0, (batch, heads, num_splits, dim)),
+            _f32_view(flat, off_m, (batch, heads, num_splits)),
+            _f32_view(flat, off_l, (batch, heads, num_splits)))

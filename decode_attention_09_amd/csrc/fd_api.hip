@@ -129,17 +129,58 @@ int check_layout(const fd_kv_layout* lay, int kv_heads, int dim, int dtype, fd_k
   return FD_OK;
 }
 
+// The two workspace formats.
+//   kNormalised: Opart [B,H,ns,D] o_s, then (256-B aligned) LSE [B,ns,H]
+//                (decode_attention_splitkv.py's part_shape / lse_shape).
+//   kUnnorm:     ACC [B,H,ns,D] acc_s, then (256-B aligned) M [B,H,ns],
+//                then (256-B aligned) L [B,H,ns] (flash_decode_splitk.py's
+//                ACC_BUF, M_BUF, L_BUF), with ceil-equal split bounds.
+enum Format { kNormalised = 0, kUnnorm = 1 };
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+  float* opart = nullptr;
+  float* lse = nullptr;
+  float* mbuf = nullptr;
+  float* lbuf = nullptr;
+};
+
+size_t workspace_bytes(Format f, int batch, int heads, int dim, int num_splits) {
+  const size_t rows = (size_t)batch * heads * num_splits;
+  const size_t opart = align256(rows * dim * sizeof(float));
+  if (f == kNormalised) return opart + rows * sizeof(float);
+  return opart + align256(rows * sizeof(float)) + rows * sizeof(float);
+}
+
+Workspace workspace_views(Format f, void* base, int batch, int heads, int dim, int num_splits) {
+  char* ws = static_cast<char*>(base);
+  const size_t rows = (size_t)batch * heads * num_splits;
+  const size_t opart = align256(rows * dim * sizeof(float));
+  Workspace w;
+  w.opart = reinterpret_cast<float*>(ws);
+  if (f == kNormalised) {
+    w.lse = reinterpret_cast<float*>(ws + opart);
+  } else {
+    w.mbuf = reinterpret_cast<float*>(ws + opart);
+    w.lbuf = reinterpret_cast<float*>(ws + opart + align256(rows * sizeof(float)));
+  }
+  return w;
+}
+
 int launch_split(const void* q, const void* k, const void* v, const int32_t* cu, int batch,
-                 int heads, int kv_heads, int dim, int num_splits, float scale, float* opart,
-                 float* lse, void* out, int direct, hipStream_t stream, int dtype,
+                 int heads, int kv_heads, int dim, int num_splits, float scale, Format fmt,
+                 const Workspace& w, void* out, int direct, hipStream_t stream, int dtype,
                  const fd_kv_layout& L, const Sizes& sz, int path) {
   fd::SplitArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.cu = cu;
-  a.opart = opart;
-  a.lse = lse;
+  a.opart = w.opart;
+  a.lse = w.lse;
+  a.mbuf = w.mbuf;
+  a.lbuf = w.lbuf;
   a.out = out;
   a.sb = L.batch_stride;
   a.sh = L.head_stride;
@@ -153,6 +194,8 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.row_chunks = sz.row_chunks;
   a.rows_per_pass = sz.rows;
   a.direct = direct;
+  a.ceil_bounds = fmt == kUnnorm ? 1 : 0;
+  a.unnorm = fmt == kUnnorm ? 1 : 0;
   a.scale_log2 = (float)((double)scale * kLog2e);
   dim3 grid((unsigned)sz.workgroups);
   const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
@@ -166,13 +209,77 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   return FD_OK;
 }
 
-// Workspace: [Opart][pad to 256 B][LSE].
-size_t opart_bytes(int batch, int heads, int dim, int num_splits) {
-  return (size_t)batch * heads * num_splits * dim * sizeof(float);
+int split_impl(Format fmt, const void* q, const void* k, const void* v,
+               const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
+               int num_splits, float scale, void* workspace, void* stream, int dtype,
+               const fd_kv_layout* layout) {
+  const int path = g_path.load(std::memory_order_relaxed);
+  Sizes sz;
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
+  if (st != FD_OK) return st;
+  if (!q || !k || !v || !cu_seqlens_k || !workspace) return FD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
+    return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  fd_kv_layout L;
+  st = check_layout(layout, kv_heads, dim, dtype, &L);
+  if (st != FD_OK) return st;
+  const Workspace w = workspace_views(fmt, workspace, batch, heads, dim, num_splits);
+  return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale, fmt,
+                      w, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path);
 }
 
-size_t lse_offset(int batch, int heads, int dim, int num_splits) {
-  return (opart_bytes(batch, heads, dim, num_splits) + 255) & ~(size_t)255;
+int combine_impl(Format fmt, const void* workspace, int batch, int heads, int dim,
+                 int num_splits, void* out, void* stream, int dtype) {
+  if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS)
+    return FD_ERR_INVALID_ARG;
+  if ((int64_t)batch * heads > INT_MAX / 2) return FD_ERR_INVALID_ARG;
+  if (dtype != FD_F32 && dtype != FD_F16 && dtype != FD_BF16) return FD_ERR_UNSUPPORTED;
+  if (!dim_ok(dim)) return FD_ERR_UNSUPPORTED;
+  if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  const Workspace w =
+      workspace_views(fmt, const_cast<void*>(workspace), batch, heads, dim, num_splits);
+  fd::CombineArgs a;
+  a.opart = w.opart;
+  a.lse = w.lse;
+  a.mbuf = w.mbuf;
+  a.lbuf = w.lbuf;
+  a.out = out;
+  a.batch = batch;
+  a.heads = heads;
+  a.num_splits = num_splits;
+  a.unnorm = fmt == kUnnorm ? 1 : 0;
+  hipError_t e = fd::launch_combine(a, dtype, dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return FD_OK;
+}
+
+int attention_impl(Format fmt, const void* q, const void* k, const void* v,
+                   const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
+                   int num_splits, float scale, void* out, void* workspace, void* stream,
+                   int dtype, const fd_kv_layout* layout) {
+  const int path = g_path.load(std::memory_order_relaxed);
+  Sizes sz;
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
+  if (st != FD_OK) return st;
+  if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
+  if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  fd_kv_layout L;
+  st = check_layout(layout, kv_heads, dim, dtype, &L);
+  if (st != FD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_splits == 1) {
+    // one split is the whole sequence under either bound rule: one launch
+    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, fmt,
+                        Workspace{}, out, 1, s, dtype, L, sz, path);
+  }
+  st = split_impl(fmt, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
+                  workspace, stream, dtype, layout);
+  if (st != FD_OK) return st;
+  return combine_impl(fmt, workspace, batch, heads, dim, num_splits, out, stream, dtype);
 }
 
 }  // namespace
@@ -182,10 +289,17 @@ extern "C" {
 size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits) {
   if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS || !dim_ok(dim))
     return 0;
-  const double est = (double)batch * heads * num_splits * (dim + 1) * 4.0;
+  const double est = (double)batch * heads * num_splits * (dim + 2) * 4.0;
   if (est > 1e18) return 0;
-  return lse_offset(batch, heads, dim, num_splits) +
-         (size_t)batch * num_splits * heads * sizeof(float);
+  return workspace_bytes(kNormalised, batch, heads, dim, num_splits);
+}
+
+size_t fd_workspace_bytes_unnorm(int batch, int heads, int dim, int num_splits) {
+  if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS || !dim_ok(dim))
+    return 0;
+  const double est = (double)batch * heads * num_splits * (dim + 2) * 4.0;
+  if (est > 1e18) return 0;
+  return workspace_bytes(kUnnorm, batch, heads, dim, num_splits);
 }
 
 int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
@@ -253,70 +367,42 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
 int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
                     int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
                     void* workspace, void* stream, int dtype, const fd_kv_layout* layout) {
-  const int path = g_path.load(std::memory_order_relaxed);
-  Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
-  if (st != FD_OK) return st;
-  if (!q || !k || !v || !cu_seqlens_k || !workspace) return FD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
-    return FD_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
-  fd_kv_layout L;
-  st = check_layout(layout, kv_heads, dim, dtype, &L);
-  if (st != FD_OK) return st;
-  char* ws = static_cast<char*>(workspace);
-  float* opart = reinterpret_cast<float*>(ws);
-  float* lse = reinterpret_cast<float*>(ws + lse_offset(batch, heads, dim, num_splits));
-  return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
-                      opart, lse, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path);
+  return split_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
+                    scale, workspace, stream, dtype, layout);
 }
 
 int fd_decode_combine(const void* workspace, int batch, int heads, int dim, int num_splits,
                       void* out, void* stream, int dtype) {
-  if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS)
-    return FD_ERR_INVALID_ARG;
-  if ((int64_t)batch * heads > INT_MAX / 2) return FD_ERR_INVALID_ARG;
-  if (dtype != FD_F32 && dtype != FD_F16 && dtype != FD_BF16) return FD_ERR_UNSUPPORTED;
-  if (!dim_ok(dim)) return FD_ERR_UNSUPPORTED;
-  if (!workspace || !out || !aligned16(workspace) || !aligned16(out)) return FD_ERR_INVALID_ARG;
-  const char* ws = static_cast<const char*>(workspace);
-  fd::CombineArgs a;
-  a.opart = reinterpret_cast<const float*>(ws);
-  a.lse = reinterpret_cast<const float*>(ws + lse_offset(batch, heads, dim, num_splits));
-  a.out = out;
-  a.batch = batch;
-  a.heads = heads;
-  a.num_splits = num_splits;
-  hipError_t e = fd::launch_combine(a, dtype, dim, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
-  return FD_OK;
+  return combine_impl(kNormalised, workspace, batch, heads, dim, num_splits, out, stream, dtype);
 }
 
 int fd_decode_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
                         int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
                         void* out, void* workspace, void* stream, int dtype,
                         const fd_kv_layout* layout) {
-  const int path = g_path.load(std::memory_order_relaxed);
-  Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
-  if (st != FD_OK) return st;
-  if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
-  if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_INVALID_ARG;
-  if (workspace && !aligned16(workspace)) return FD_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
-  fd_kv_layout L;
-  st = check_layout(layout, kv_heads, dim, dtype, &L);
-  if (st != FD_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (num_splits == 1) {
-    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, nullptr,
-                        nullptr, out, 1, s, dtype, L, sz, path);
-  }
-  st = fd_decode_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
-                       workspace, stream, dtype, layout);
-  if (st != FD_OK) return st;
-  return fd_decode_combine(workspace, batch, heads, dim, num_splits, out, stream, dtype);
+  return attention_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim,
+                        num_splits, scale, out, workspace, stream, dtype, layout);
+}
+
+int fd_decode_split_unnorm(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads,
+                           int dim, int num_splits, float scale, void* workspace, void* stream,
+                           int dtype, const fd_kv_layout* layout) {
+  return split_impl(kUnnorm, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
+                    scale, workspace, stream, dtype, layout);
+}
+
+int fd_decode_combine_unnorm(const void* workspace, int batch, int heads, int dim,
+                             int num_splits, void* out, void* stream, int dtype) {
+  return combine_impl(kUnnorm, workspace, batch, heads, dim, num_splits, out, stream, dtype);
+}
+
+int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads,
+                               int dim, int num_splits, float scale, void* out, void* workspace,
+                               void* stream, int dtype, const fd_kv_layout* layout) {
+  return attention_impl(kUnnorm, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
+                        scale, out, workspace, stream, dtype, layout);
 }
 
 const char* fd_status_string(int status) {

@@ -5,24 +5,33 @@
 
 namespace fd {
 
-// The LSE merge of one (sequence, head) by a workgroup of NWAVES waves:
-//   M = max_s lse_s, lse = M + log2 sum_s 2^(lse_s - M),
-//   o = sum_s 2^(lse_s - lse) * o_s,   rounded to the dtype,
-// the combine segment of gqa_decode_splitkv in "decode_attention_splitkv.py"
-// (TileLang tutorial, ch. 18), with the weight of split s for a head applied
-// to that head's row, and the merge of "04_flash_decoding.py" (CS349E
-// lecture 11), demo 1.
+// The merge of one (sequence, head) by a workgroup of NWAVES waves.
 //
-// Each wave owns a strided subset of the partial rows (SPW rows side by
-// side, D/64 dims per lane when D >= 64). Every load the merge needs is
-// issued up front -- one LSE per thread for the max and the sum, and the
-// first KR partial rows of each lane group with their LSEs -- so the whole
-// merge waits for memory once; rows beyond KR (many splits) are read after
-// the reductions. The waves' maxima, sums and row sums meet in LDS. All
-// threads of the workgroup must call it (it synchronises).
-template <int DT, int D, int NWAVES>
-__device__ __forceinline__ void combine_head(const float* opart, const float* lse_base, void* out,
-                                             int heads, int ns, int b, int h) {
+// Normalised format (UNNORM = false), the combine segment of
+// gqa_decode_splitkv in "decode_attention_splitkv.py" (TileLang tutorial,
+// ch. 18) and the merge of "04_flash_decoding.py" (CS349E lecture 11),
+// demo 1, with the weight of split s for a head applied to that head's row:
+//   M = max_s lse_s, lse = M + log2 sum_s 2^(lse_s - M),
+//   o = sum_s 2^(lse_s - lse) * o_s.
+// Unnormalised format (UNNORM = true), _splitk_reduce_kernel of
+// "flash_decode_splitk.py" (MiniInfer):
+//   M = max_s m_s, alpha_s = 2^(m_s - M),
+//   o = sum_s alpha_s acc_s / sum_s alpha_s l_s.
+// Either way o is rounded to the dtype; a row whose splits are all empty
+// (every key -inf) is written as zeros.
+//
+// key[s * kst] is lse_s or m_s, lw[s * kst] is l_s (unnormalised format),
+// op[s * D + d] the partial row of split s. Each wave owns a strided subset
+// of the partial rows (SPW rows side by side, D/64 dims per lane when
+// D >= 64). Every load the merge needs is issued up front -- one key (and l)
+// per thread for the max and the sum, and the first KR partial rows of each
+// lane group with their keys -- so the merge waits for memory once; rows
+// beyond KR (many splits) are read after the reductions. The waves' maxima,
+// sums and row sums meet in LDS. All threads of the workgroup must call it
+// (it synchronises).
+template <int DT, int D, int NWAVES, bool UNNORM>
+__device__ __forceinline__ void combine_head(const float* op, const float* key, const float* lw,
+                                             int64_t kst, int ns, void* out, int64_t bh) {
   constexpr int NT = kWave * NWAVES;
   constexpr int DPL = D >= kWave ? D / kWave : 1;  // dims per lane
   constexpr int LPS = D / DPL;                     // lanes per partial row
@@ -35,27 +44,25 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int64_t bh = (int64_t)b * heads + h;
-  const float* lse = lse_base + (int64_t)b * ns * heads + h;  // split stride = heads
-  const float* op = opart + bh * ns * D;
   const int sg = lane / LPS;
   const int dl = lane % LPS;
   const int s0 = wave * SPW + sg;  // first partial row of this lane group
 
   // every load up front
-  const float l_own = tid < ns ? lse[(int64_t)tid * heads] : kNegInf;
-  float pl[KR], pv[KR][DPL];
+  const float k_own = tid < ns ? key[(int64_t)tid * kst] : kNegInf;
+  const float l_own = UNNORM && tid < ns ? lw[(int64_t)tid * kst] : 0.0f;
+  float pk[KR], pv[KR][DPL];
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
     const int s = s0 + k * RPG;
     const bool in = s < ns;
-    pl[k] = in ? lse[(int64_t)s * heads] : kNegInf;
+    pk[k] = in ? key[(int64_t)s * kst] : kNegInf;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) pv[k][e] = in ? op[(int64_t)s * D + dl * DPL + e] : 0.0f;
   }
 
-  float mx = l_own;
-  for (int s = tid + NT; s < ns; s += NT) mx = fmaxf(mx, lse[(int64_t)s * heads]);
+  float mx = k_own;
+  for (int s = tid + NT; s < ns; s += NT) mx = fmaxf(mx, key[(int64_t)s * kst]);
   mx = across_groups<1>(mx, OpMax{});
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -69,18 +76,28 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
 
   if (mx != kNegInf) {  // uniform: every split empty -> zero row
-    float tot = l_own == kNegInf ? 0.0f : fast_exp2(l_own - mx);
-    for (int s = tid + NT; s < ns; s += NT) tot += fast_exp2(lse[(int64_t)s * heads] - mx);
+    // tot = sum_s 2^(key_s - mx) (times l_s in the unnormalised format)
+    float tot = k_own == kNegInf ? 0.0f : fast_exp2(k_own - mx) * (UNNORM ? l_own : 1.0f);
+    for (int s = tid + NT; s < ns; s += NT) {
+      const float x = fast_exp2(key[(int64_t)s * kst] - mx);
+      tot += UNNORM ? x * lw[(int64_t)s * kst] : x;
+    }
     tot = across_groups<1>(tot, OpAdd{});
     if (lane == 0) red[wave] = tot;
     __syncthreads();
     tot = 0.0f;
 #pragma unroll
     for (int w = 0; w < NWAVES; ++w) tot += red[w];
+    // weight of split s: 2^(key_s - lse) = 2^(key_s - mx) / tot, written
+    // as the page's formula of each format
     const float lse_all = mx + fast_log2(tot);
+    const float inv_tot = 1.0f / tot;
+    auto weight = [&](float ks) {
+      return UNNORM ? fast_exp2(ks - mx) * inv_tot : fast_exp2(ks - lse_all);
+    };
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
-      const float wt = fast_exp2(pl[k] - lse_all);  // 0 for rows past ns
+      const float wt = weight(pk[k]);  // 0 for rows past ns
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(wt, pv[k][e], acc[e]);
     }
@@ -90,7 +107,7 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
       float v[4][DPL];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wt[u] = fast_exp2(lse[(int64_t)(s + u * RPG) * heads] - lse_all);
+        wt[u] = weight(key[(int64_t)(s + u * RPG) * kst]);
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
           v[u][e] = op[(int64_t)(s + u * RPG) * D + dl * DPL + e];
@@ -101,7 +118,7 @@ __device__ __forceinline__ void combine_head(const float* opart, const float* ls
         for (int e = 0; e < DPL; ++e) acc[e] = __builtin_fmaf(wt[u], v[u][e], acc[e]);
     }
     for (; s < ns; s += RPG) {
-      const float wt = fast_exp2(lse[(int64_t)s * heads] - lse_all);
+      const float wt = weight(key[(int64_t)s * kst]);
 #pragma unroll
       for (int e = 0; e < DPL; ++e)
         acc[e] = __builtin_fmaf(wt, op[(int64_t)s * D + dl * DPL + e], acc[e]);
@@ -127,9 +144,19 @@ constexpr int kCombineWaves = 4;
 // One workgroup of four waves per (sequence, head).
 template <int DT, int D>
 __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineArgs a) {
-  const int bh = blockIdx.x;
-  combine_head<DT, D, kCombineWaves>(a.opart, a.lse, a.out, a.heads, a.num_splits,
-                                     bh / a.heads, bh % a.heads);
+  const int64_t bh = blockIdx.x;
+  const int ns = a.num_splits;
+  const float* op = a.opart + bh * ns * D;
+  if (a.unnorm) {
+    // m_s, l_s at [B, H, ns]
+    combine_head<DT, D, kCombineWaves, true>(op, a.mbuf + bh * ns, a.lbuf + bh * ns, 1, ns,
+                                             a.out, bh);
+  } else {
+    // lse_s at [B, ns, H]: split stride = heads
+    const int64_t b = bh / a.heads, h = bh % a.heads;
+    combine_head<DT, D, kCombineWaves, false>(op, a.lse + b * ns * a.heads + h, nullptr,
+                                              a.heads, ns, a.out, bh);
+  }
 }
 
 template <int DT, int D>

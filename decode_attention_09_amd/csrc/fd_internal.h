@@ -27,21 +27,28 @@ struct SplitArgs {
   const void* k;
   const void* v;
   const int32_t* cu;
-  float* opart;     // [B, H, ns, D] fp32 (workspace mode)
-  float* lse;       // [B, ns, H]   fp32 (workspace mode)
+  float* opart;     // [B, H, ns, D] fp32 (workspace mode): o_s, or acc_s if unnorm
+  float* lse;       // [B, ns, H]   fp32 (workspace mode, normalised format)
+  float* mbuf;      // [B, H, ns]   fp32 (workspace mode, unnorm format): m_s
+  float* lbuf;      // [B, H, ns]   fp32 (workspace mode, unnorm format): l_s
   void* out;        // [B, H, D] dtype (direct mode, ns == 1)
   int64_t sb, sh, st, scu;  // K/V strides in elements: batch, head, token, cu
   int batch, heads, kv_heads, group, num_splits, row_chunks;
   int rows_per_pass; // query rows of a group per workgroup (<= the kernel's rows)
-  int direct;       // 1: write out in dtype; 0: write opart/lse
+  int direct;       // 1: write out in dtype; 0: write the workspace
+  int ceil_bounds;  // 1: ceil-equal split bounds; 0: proportional
+  int unnorm;       // 1: workspace holds (m, l, acc); 0: (o_s, lse2_s)
   float scale_log2; // scale * log2(e)
 };
 
 struct CombineArgs {
-  const float* opart;
-  const float* lse;
+  const float* opart;  // o_s, or acc_s (unnorm)
+  const float* lse;    // [B, ns, H] (normalised format)
+  const float* mbuf;   // [B, H, ns] (unnorm format)
+  const float* lbuf;   // [B, H, ns] (unnorm format)
   void* out;
   int batch, heads, num_splits;
+  int unnorm;
 };
 
 // Launchers (defined in fd_split_<dtype>.hip and fd_combine.hip). They

@@ -1,7 +1,9 @@
 // Split kernel of flash decoding for gfx950: one workgroup per
 // (split, KV head, row chunk, sequence) computes, for the packed query rows
 // of one GQA group, the online-softmax partial output of its KV segment and
-// the segment's base-2 log-sum-exp.
+// the segment's base-2 log-sum-exp -- or, in the format of
+// "flash_decode_splitk.py" (MiniInfer), the segment's unnormalised state
+// (max, sum, accumulator) over ceil-equal split bounds.
 //
 // Behaviour follows the split segment of gqa_decode_splitkv in
 // "decode_attention_splitkv.py" (TileLang tutorial, ch. 18): varlen bounds
@@ -22,7 +24,10 @@
 //  * Online softmax per lane group (the RPI keys rows of a load are handled
 //    by different lane groups, each with its own running max), rescaling
 //    lazily: the reference max only moves when a tile exceeds it by more
-//    than 2^8, so rescaling is rare and p stays <= 256.
+//    than 2^8, so rescaling is rare and p stays <= 256. The true max is
+//    tracked beside it, and the end-of-segment merge rescales every lane
+//    group onto it, so the written state refers to the segment's largest
+//    score (the MiniInfer format stores it as m_s).
 //  * PV: p for two keys is packed to fp16x2/bf16x2 and multiplied with the
 //    matching pair of V elements (v_perm regroups them) by v_dot2, fp32 acc.
 //  * Bounds: each tile's K/V loads go through a buffer descriptor whose
@@ -288,8 +293,17 @@ __device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const Work
   }
   const int ns = a.num_splits;
   const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
-  const int64_t seg0 = L * g.sid / ns;
-  g.nkeys = L * (g.sid + 1) / ns - seg0;
+  int64_t seg0, seg1;
+  if (a.ceil_bounds) {
+    // ceil-equal: size = ceil(L/ns) from sid*size, cut at L (may be empty)
+    const int64_t size = (L + ns - 1) / ns;
+    seg0 = min(size * g.sid, L);
+    seg1 = min(size * g.sid + size, L);
+  } else {
+    seg0 = L * g.sid / ns;
+    seg1 = L * (g.sid + 1) / ns;
+  }
+  g.nkeys = seg1 - seg0;
   const int64_t row0 =
       (int64_t)g.b * a.sb + (int64_t)cu0 * a.scu + (int64_t)g.kvh * a.sh + seg0 * a.st;
   g.k = static_cast<const char*>(a.k) + row0 * EB;
@@ -313,7 +327,9 @@ __device__ __forceinline__ void tile_rsrc(const Segment& sg, int j, __amdgpu_buf
 
 // Merge the per-wave states (max, sum, unnormalised acc) left in LDS and
 // write the split epilogue: o_s = acc / l and lse2_s = log2(l) + m, or the
-// final output in dtype when the call has a single split.
+// unnormalised state (m_s, l_s, acc_s) of the MiniInfer format (m_s the
+// split's largest base-2 score), or the final output in dtype when the call
+// has a single split.
 template <int DT, int D, int GC, int NW>
 __device__ __forceinline__ void store_segment(const SplitArgs& a, const Segment& sg,
                                               const float (&sm_m)[NW][GC],
@@ -334,12 +350,18 @@ __device__ __forceinline__ void store_segment(const SplitArgs& a, const Segment&
       o += f * sm_acc[w][g][d];
     }
     const bool any = lsum > 0.0f;
-    o = any ? o / lsum : 0.0f;
     const int h = sg.h0 + g;
+    const int64_t row = ((int64_t)sg.b * a.heads + h) * ns + sg.sid;  // [B, H, ns]
     if (a.direct) {
-      store_out<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, o);
+      store_out<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, any ? o / lsum : 0.0f);
+    } else if (a.unnorm) {
+      a.opart[row * D + d] = o;
+      if (d == 0) {
+        a.mbuf[row] = M;  // -inf for an empty split
+        a.lbuf[row] = lsum;
+      }
     } else {
-      a.opart[(((int64_t)sg.b * a.heads + h) * ns + sg.sid) * D + d] = o;
+      a.opart[row * D + d] = any ? o / lsum : 0.0f;
       if (d == 0)
         a.lse[((int64_t)sg.b * ns + sg.sid) * a.heads + h] = any ? fast_log2(lsum) + M : kNegInf;
     }
@@ -429,7 +451,8 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
   const uint32_t tsb = (uint32_t)(a.st * EB);
   const uint32_t lane_off = (uint32_t)rg * tsb + (uint32_t)c * 16u;
 
-  float m[GC], l[GC], acc[GC][EPL];
+  // m: the lazily moved reference max of each lane group; mt: the true max
+  float m[GC], mt[GC], l[GC], acc[GC][EPL];
   Segment sg;  // the current item's segment
   struct Tile {
     u4_t k[NI], v[NI];
@@ -465,6 +488,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
       float tmax = s[0][g];
 #pragma unroll
       for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, s[i][g]);
+      mt[g] = fmaxf(mt[g], tmax);
       if (tmax > m[g] + kLazyRescale) {
         const float alpha = fast_exp2(m[g] - tmax);
         l[g] *= alpha;
@@ -527,6 +551,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
     m[g] = kNegInf;
+    mt[g] = kNegInf;
     l[g] = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
@@ -534,10 +559,10 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
   const int nt = (int)((sg.nkeys + TK - 1) / TK);
   tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
-  // ---- merge the lane groups of this wave (each has its own max) ----
+  // ---- merge the lane groups of this wave onto the wave's true max ----
 #pragma unroll
   for (int g = 0; g < GC; ++g) {
-    const float M = across_groups<LPR>(m[g], OpMax{});
+    const float M = across_groups<LPR>(mt[g], OpMax{});
     const float f = m[g] == kNegInf ? 0.0f : fast_exp2(m[g] - M);
     l[g] = across_groups<LPR>(l[g] * f, OpAdd{});
 #pragma unroll
@@ -639,7 +664,9 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
   const uint32_t k_off = (uint32_t)c * tsb + (uint32_t)R * 16u;       // + 64*m
   const uint32_t v_off = (uint32_t)(4 * R) * tsb + (uint32_t)c * 16u;  // + i*tsb
 
-  float m_run, l_run;  // for (key group R, query row c)
+  // for (key group R, query row c): the lazily moved reference max, the
+  // true max, and the sum relative to the reference
+  float m_run, m_true, l_run;
   float acc[GC][8];
   Segment sg;  // the current item's segment
   struct Tile {
@@ -671,6 +698,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
       s[r] = valid[r] ? s4[r] * a.scale_log2 : kNegInf;
     }
     const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    m_true = fmaxf(m_true, tmax);
     const bool need = tmax > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {  // uniform, rare after the first tile
       float alpha = 1.0f;
@@ -720,6 +748,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
   if (sg.b != wi.rank) load_q(wi, sg.b);
   load_tile_of(sg, wave, buf[0]);
   m_run = kNegInf;
+  m_true = kNegInf;
   l_run = 0.0f;
 #pragma unroll
   for (int g = 0; g < GC; ++g)
@@ -728,8 +757,8 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
   const int nt = (int)((sg.nkeys + TK - 1) / TK);
   tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
-  // ---- merge the four key groups R of this wave ----
-  const float M = across_groups<16>(m_run, OpMax{});
+  // ---- merge the four key groups R of this wave onto its true max ----
+  const float M = across_groups<16>(m_true, OpMax{});
   const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
   const float lw = across_groups<16>(l_run * f, OpAdd{});
   static_for<GC>([&](auto gi) {

@@ -172,6 +172,59 @@ int fd_decode_combine(const void* workspace, int batch, int heads, int dim,
                       int num_splits, void* out, void* stream, int dtype);
 
 /*
+ * The second workspace format, that of _splitk_stage1_kernel and
+ * _splitk_reduce_kernel in "flash_decode_splitk.py" (MiniInfer):
+ *
+ *   - split bounds are ceil-equal: with size = ceil(L_b / num_splits),
+ *     split s covers keys [s*size, min(s*size + size, L_b)); splits that
+ *     start at or past L_b are empty, which is allowed (any num_splits in
+ *     1..FD_MAX_SPLITS, whatever the lengths);
+ *   - every split leaves its unnormalised state, with s2_t = scale *
+ *     log2(e) * q.k_t the base-2 scaled scores of its keys:
+ *       m_s   = max_t s2_t                      (-inf for an empty split)
+ *       l_s   = sum_t 2^(s2_t - m_s)            (0 for an empty split)
+ *       acc_s = sum_t 2^(s2_t - m_s) * v_t      (0 for an empty split)
+ *   - the combine rescales to M = max_s m_s:
+ *       o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,
+ *     and writes zeros for a row whose splits are all empty.
+ *
+ * The result is the same attention as fd_decode_attention's (same
+ * tolerances); only the bounds and the partials differ. Arguments,
+ * alignment, layout, ownership and error codes are those of the
+ * corresponding functions above.
+ *
+ * fd_workspace_bytes_unnorm -- fp32 workspace of the unnormalised format:
+ *   ACC [batch, heads, num_splits, dim]   acc_s
+ *   M   [batch, heads, num_splits]        m_s   (first 256-B boundary after ACC)
+ *   L   [batch, heads, num_splits]        l_s   (first 256-B boundary after M)
+ * the layouts of ACC_BUF ([bh, ns, dim]) and M_BUF / L_BUF ([bh, ns]). 0 on
+ * bad sizes.
+ */
+size_t fd_workspace_bytes_unnorm(int batch, int heads, int dim, int num_splits);
+
+/* fd_decode_split_unnorm -- split launch only, writing (ACC, M, L) into
+ * `workspace` (fd_workspace_bytes_unnorm bytes, required). */
+int fd_decode_split_unnorm(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_k, int batch, int heads,
+                           int kv_heads, int dim, int num_splits, float scale,
+                           void* workspace, void* stream, int dtype,
+                           const fd_kv_layout* layout);
+
+/* fd_decode_combine_unnorm -- combine launch only, from an (ACC, M, L)
+ * workspace into out [batch, heads, dim] dtype. */
+int fd_decode_combine_unnorm(const void* workspace, int batch, int heads, int dim,
+                             int num_splits, void* out, void* stream, int dtype);
+
+/* fd_decode_attention_unnorm -- split + combine in this format. With
+ * num_splits == 1 one launch writes `out` directly and `workspace` may be
+ * NULL (one split is the whole sequence under either bound rule). */
+int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_k, int batch, int heads,
+                               int kv_heads, int dim, int num_splits, float scale,
+                               void* out, void* workspace, void* stream, int dtype,
+                               const fd_kv_layout* layout);
+
+/*
  * fd_set_kernel_path -- which split kernel later calls launch, process-wide
  * (for benchmarks and tests that compare the two; calls already enqueued are
  * unaffected). FD_PATH_VALU: vector-ALU dot products (v_dot2 / FMA) for

@@ -31,7 +31,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
-              "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path"):
+              "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path",
+              "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
+              "fd_decode_attention_unnorm"):
         assert n in names
 
 
@@ -60,6 +62,18 @@ def test_workspace_bytes_layout(B, H, D, ns):
     opart = B * H * ns * D * 4
     lse_off = (opart + 255) // 256 * 256
     assert n == lse_off + B * ns * H * 4
+
+
+@pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (3, 5, 64, 1000)])
+def test_workspace_bytes_unnorm_layout(B, H, D, ns):
+    # ACC [B,H,ns,D], then M [B,H,ns] and L [B,H,ns], each at a 256-B boundary
+    n = fd.fd_workspace_bytes_unnorm(B, H, D, ns)
+    rows = B * H * ns
+    off_m = (rows * D * 4 + 255) // 256 * 256
+    off_l = off_m + (rows * 4 + 255) // 256 * 256
+    assert n == off_l + rows * 4
+    assert fd.fd_workspace_bytes_unnorm(0, H, D, ns) == 0
+    assert fd.fd_workspace_bytes_unnorm(B, H, 96, ns) == 0
 
 
 def test_workspace_bytes_rejects_bad_sizes():
@@ -178,6 +192,26 @@ def test_layout_checks():
            fd.FdKvLayout(0, 128, 1 << 23, 0)]  # tile offsets would not fit 32 bits
     for lay in bad:
         assert _attn(lib, lay=ctypes.byref(lay)) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(out=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 1), (dict(H=9, Hkv=2), 1), (dict(ns=0), 1), (dict(scale=float("nan")), 1),
+    (dict(D=96), 2), (dict(dt=7), 2),
+])
+def test_unnorm_attention_rejects_before_launch(kw, status):
+    lib = _lib()
+    base = dict(q=16, k=16, v=16, cu=16, B=1, H=8, Hkv=1, D=128, ns=2, scale=0.1, out=16,
+                ws=16, stream=None, dt=fd.FD_F16, lay=None)
+    base.update(kw)
+    assert lib.fd_decode_attention_unnorm(
+        base["q"], base["k"], base["v"], base["cu"], base["B"], base["H"], base["Hkv"],
+        base["D"], base["ns"], base["scale"], base["out"], base["ws"], base["stream"],
+        base["dt"], base["lay"]) == status
+    assert lib.fd_decode_split_unnorm(16, 16, 16, 16, 1, 8, 1, 128, 2, 0.1, None, None, 1,
+                                      None) == 1
+    assert lib.fd_decode_combine_unnorm(None, 1, 8, 128, 2, 16, None, 1) == 1
+    assert lib.fd_decode_combine_unnorm(16, 1, 8, 64 + 32, 2, 16, None, 1) == 2
 
 
 def test_split_and_combine_reject_before_launch():
