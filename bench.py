@@ -79,11 +79,11 @@ def traffic_for(workload_name: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, ns, budget_s: float, fmt: str = "lse"):
+def cpu_baseline(inp, ns, budget_s: float, fmt: str = "lse", threads: int = 1):
     """The fp64 numpy oracle (split + merge) on the same workload, one
     (sequence, KV head) unit at a time in order, repeated until its own
-    compute time reaches ~budget_s seconds; BLAS limited to one thread.
-    Host copies of the inputs are made outside the clock."""
+    compute time reaches ~budget_s seconds; BLAS limited to `threads`
+    threads. Host copies of the inputs are made outside the clock."""
     from threadpoolctl import threadpool_limits
     import oracle
     w = inp.workload
@@ -95,7 +95,7 @@ def cpu_baseline(inp, ns, budget_s: float, fmt: str = "lse"):
     done_bytes = 0
     n_units = 0
     oracle_s = 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while oracle_s < budget_s:
             b, j = units[n_units % len(units)]
             L = cu[b + 1] - cu[b]
@@ -120,7 +120,7 @@ def cpu_baseline(inp, ns, budget_s: float, fmt: str = "lse"):
     return {
         "value": round(done_bytes / oracle_s / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{n_units} (sequence, KV head) units of this workload "
                   f"({n_units / len(units):.2f} passes), fp64 split+merge, "
@@ -187,6 +187,19 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     # the dominant kernel: with one split the whole step is that one launch;
     # otherwise the split kernel alone, same inputs and launch configuration
     split_avg = ms_per_step if single_launch else timed(split_only, steps, warmup + steps)[0]
+    # per-call spread: an event pair around each call (the events add a
+    # little to each call, so the mean above is the headline)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        step(warmup + 2 * steps + i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+
+    def pct(p):
+        return round(per_call[min(len(per_call) - 1, int(p * len(per_call)))], 3)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (split_avg * 1e-3) / 1e9
     res = {
@@ -198,6 +211,8 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_call": round(ms_per_step * 1e3, 3),
+        "per_call_us": {"p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90), "calls": steps,
+                        "how": "HIP events around each call"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -221,6 +236,9 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     }
     if cpu_s > 0:
         res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s, fmt)
+        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        if threads > 1:
+            res["cpu_baseline_all_cores"] = cpu_baseline(inp, ns, cpu_s, fmt, threads)
     return res
 
 
