@@ -271,3 +271,20 @@ def test_whole_call_matches_split_then_combine_over_many_calls(lens, heads, kvh,
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("lens", [[16384], [20000, 16390]])
+def test_maximum_split_count(lens):
+    """FD_MAX_SPLITS splits: one key per split at L = 16384, ragged sizes
+    above it; the combine walks 16384 partial rows per head."""
+    fd = H.fd()
+    ns = fd.FD_MAX_SPLITS
+    inp = _rand_inputs(lens, 8, 1, 128, "f16", seed=21)
+    out = H.host(H.gpu_attention(inp, ns))
+    assert H.max_err(out, H.oracle_full(inp, None)) <= H.TOL["f16"]
+    ws, opart, lse2 = H.gpu_split(inp, ns)
+    q, k, v = H.host(inp.q), H.host(inp.k), H.host(inp.v)
+    op_ref, lse_ref = oracle.attention_partials(q, k, v, inp.cu_seqlens_k.cpu().tolist(), 8, 1,
+                                                ns, inp.workload.sm_scale)
+    assert H.max_err(opart, op_ref) <= H.TOL["f16"]
+    assert H.max_err(lse2, lse_ref * H.LOG2E) <= 1e-4

@@ -260,3 +260,10 @@ def test_all_empty_sequences_give_zero_rows():
     for ns in (1, 3):
         out = H.host(gpu_attention_unnorm(inp, ns))
         assert not out.any()
+
+
+def test_maximum_split_count_unnorm():
+    """FD_MAX_SPLITS ceil-equal splits over 20,000 and 9,000 keys: size 2,
+    so the shorter sequence leaves thousands of empty tail splits."""
+    ns = H.fd().FD_MAX_SPLITS
+    compare_states(_rand([20000, 9000], 8, 1, 128, "f16", seed=22), ns)
