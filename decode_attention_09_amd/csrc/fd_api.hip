@@ -197,6 +197,14 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.ceil_bounds = fmt == kUnnorm ? 1 : 0;
   a.unnorm = fmt == kUnnorm ? 1 : 0;
   a.scale_log2 = (float)((double)scale * kLog2e);
+  // Non-temporal K/V loads pay off once the launch fills every compute unit
+  // (measured; below that each workgroup's stream is latency-bound and they
+  // slow it). The unpacked comparison path re-reads K/V once per query head
+  // and keeps the default policy, under which those re-reads can hit cache.
+  int cus = 0;
+  const int cst = device_cus(&cus);
+  if (cst != FD_OK) return cst;
+  a.kv_nt = path != FD_PATH_UNPACKED && sz.workgroups >= cus ? 1 : 0;
   dim3 grid((unsigned)sz.workgroups);
   const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;

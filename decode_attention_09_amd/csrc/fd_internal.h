@@ -35,6 +35,7 @@ struct SplitArgs {
   int64_t sb, sh, st, scu;  // K/V strides in elements: batch, head, token, cu
   int batch, heads, kv_heads, group, num_splits, row_chunks;
   int rows_per_pass; // query rows of a group per workgroup (<= the kernel's rows)
+  int kv_nt;        // 1: K/V loads with the non-temporal cache policy
   int direct;       // 1: write out in dtype; 0: write the workspace
   int ceil_bounds;  // 1: ceil-equal split bounds; 0: proportional
   int unnorm;       // 1: workspace holds (m, l, acc); 0: (o_s, lse2_s)
