@@ -669,8 +669,15 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
     }
   };
   const uint32_t tsb = (uint32_t)(a.st * EB);
-  const uint32_t k_off = (uint32_t)c * tsb + (uint32_t)R * 16u;       // + 64*m
-  const uint32_t v_off = (uint32_t)(4 * R) * tsb + (uint32_t)c * 16u;  // + i*tsb
+  // K and V are both loaded as whole rows: lane (R, c) gets 16-byte chunk c
+  // of rows 4R + i, i = 0..3 (one wave-wide load = 4 full 256-byte rows).
+  const uint32_t kv_off = (uint32_t)(4 * R) * tsb + (uint32_t)c * 16u;  // + i*tsb
+  // K is regrouped through LDS into the matrix-core layout: row stride 17
+  // chunks (272 bytes) keeps both the writes and the reads free of bank
+  // conflicts.
+  constexpr int kLdsRow = 17;
+  __shared__ u4_t lds_k[NW][16 * kLdsRow];
+  u4_t* const my_k = lds_k[wave];
 
   // for (key group R, query row c): the lazily moved reference max, the
   // true max, and the sum relative to the reference
@@ -684,16 +691,24 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc<TK, D * EB>(sgx, j, rk, rv);
 #pragma unroll
-    for (int m = 0; m < KS; ++m) t.k[m] = buffer_load16<NT>(rk, k_off + 64u * m);
+    for (int i = 0; i < KS; ++i) t.k[i] = buffer_load16<NT>(rk, kv_off + (uint32_t)i * tsb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16<NT>(rv, v_off + (uint32_t)i * tsb);
+    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16<NT>(rv, kv_off + (uint32_t)i * tsb);
   };
   auto load_tile = [&](int j, Tile& t) { load_tile_of(sg, j, t); };
 
   auto compute_tile = [&](int j, const Tile& t) {
-    const u4_t(&kt)[KS] = t.k;
     const u4_t(&vt)[4] = t.v;
     const int64_t nkeys = sg.nkeys;
+    // K rows 4R + i, chunk c -> LDS -> lane (R, c) takes chunk 4m + R of
+    // row c for MFMA step m (the k order is the same for Q, see load_q).
+    // One wave writes and reads its own slice; LDS instructions of a wave
+    // complete in order, so no barrier is needed.
+#pragma unroll
+    for (int i = 0; i < KS; ++i) my_k[(4 * R + i) * kLdsRow + c] = t.k[i];
+    u4_t kt[KS];
+#pragma unroll
+    for (int m = 0; m < KS; ++m) kt[m] = my_k[c * kLdsRow + 4 * m + R];
     f4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < KS; ++m) s4 = mfma_qk<DT>(kt[m], qb[m], s4);
