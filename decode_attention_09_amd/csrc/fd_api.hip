@@ -26,11 +26,13 @@ thread_local char g_last_error[256] = "";
 std::atomic<int> g_path{FD_PATH_AUTO};
 
 // The library's own choice of split kernel: matrix-core QK^T wherever that
-// kernel exists (16-bit inputs, head dim 128). Measured on MI355X it is
-// faster at groups of 4-8 (2.4x fewer VALU instructions) and no slower at 1.
+// kernel exists (16-bit inputs, head dim 128) and the group has at least 2
+// query heads. Measured on MI355X with both kernels streaming whole K/V rows:
+// the matrix-core kernel is 0-15 % faster at groups 2-8 (2.5-2.8x fewer VALU
+// instructions at 4-8), while at group 1 -- one valid column of its 16 --
+// the VALU kernel is 1-5 % faster.
 bool auto_mfma(int dtype, int dim, int group) {
-  (void)group;
-  return dtype != FD_F32 && dim == 128;
+  return dtype != FD_F32 && dim == 128 && group >= 2;
 }
 
 int hip_fail(hipError_t e, const char* where) {
