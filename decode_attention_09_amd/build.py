@@ -38,7 +38,7 @@ def hipcc() -> str:
 
 
 def _flags():
-    # FD_HIPCC_FLAGS: extra hipcc flags (e.g. -DFD_PREFETCH_TILES=2)
+    # FD_HIPCC_FLAGS: extra hipcc flags (e.g. -DFD_PREFETCH_TILES_VALU=2)
     return FLAGS + os.environ.get("FD_HIPCC_FLAGS", "").split()
 
 

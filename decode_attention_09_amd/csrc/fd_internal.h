@@ -15,11 +15,16 @@ constexpr int kWavesPerGroup = FD_WAVES_PER_GROUP;  // waves per split workgroup
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
 constexpr int kLptMaxBatch = 64;   // batches up to this size run longest sequence first
 constexpr int kLoadsPerTile = 4;   // 16-byte K (and V) loads per lane per tile
-#ifndef FD_PREFETCH_TILES
-#define FD_PREFETCH_TILES 1
+#ifndef FD_PREFETCH_TILES_VALU
+#define FD_PREFETCH_TILES_VALU 1
 #endif
-// Tiles whose loads are in flight while a wave computes the current one.
-constexpr int kPrefetchTiles = FD_PREFETCH_TILES;
+#ifndef FD_PREFETCH_TILES_MFMA
+#define FD_PREFETCH_TILES_MFMA 1
+#endif
+// Tiles whose loads are in flight while a wave computes the current one,
+// for the VALU and the matrix-core split kernel.
+constexpr int kPrefetchTilesValu = FD_PREFETCH_TILES_VALU;
+constexpr int kPrefetchTilesMfma = FD_PREFETCH_TILES_MFMA;
 
 // Arguments of the split kernel (passed by value).
 struct SplitArgs {

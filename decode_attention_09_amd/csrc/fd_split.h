@@ -36,8 +36,9 @@
 //    masked out of the softmax.
 //  * Four waves per workgroup take interleaved tiles of the segment and are
 //    merged through LDS at the end (the same LSE merge as the combine).
-//  * Register tile pipeline: the loads of the next kPrefetchTiles tiles are
-//    in flight while the current tile is computed.
+//  * Register tile pipeline: the loads of the next kPrefetchTilesValu
+//    (kPrefetchTilesMfma) tiles are in flight while the current tile is
+//    computed.
 #pragma once
 
 #include <type_traits>
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     }
   };
 
-  Tile buf[kPrefetchTiles + 1];
+  Tile buf[kPrefetchTilesValu + 1];
   const WorkItem wi = decode_item<GC>(a, blockIdx.x);
   load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
   sg = locate_segment<EB>(a, wi, ls);
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
   }
   const int nt = (int)((sg.nkeys + TK - 1) / TK);
-  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+  tile_pipeline<kPrefetchTilesValu, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
   // ---- merge the lane groups of this wave onto the wave's true max ----
 #pragma unroll
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
     }
   };
 
-  Tile buf[kPrefetchTiles + 1];
+  Tile buf[kPrefetchTilesMfma + 1];
   const WorkItem wi = decode_item<GC>(a, blockIdx.x);
   load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
   sg = locate_segment<EB>(a, wi, ls);
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(Split
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   const int nt = (int)((sg.nkeys + TK - 1) / TK);
-  tile_pipeline<kPrefetchTiles, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+  tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
   // ---- merge the four key groups R of this wave onto its true max ----
   const float M = across_groups<16>(m_true, OpMax{});
