@@ -14,7 +14,18 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kWavesPerGroup = FD_WAVES_PER_GROUP;  // waves per split workgroup
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
 constexpr int kLptMaxBatch = 64;   // batches up to this size run longest sequence first
-constexpr int kLoadsPerTile = 4;   // 16-byte K (and V) loads per lane per tile
+#ifndef FD_LOADS_PER_TILE
+#define FD_LOADS_PER_TILE 4
+#endif
+// 16-byte K (and V) loads per lane per VALU tile. 16-bit rows of head dim
+// <= 32 take 2: measured on MI355X (MHA, 4 x 32 heads x 4K keys) the split
+// kernel goes from 11.0 to 9.6 us at D = 16 and from 14.9 to 13.6 us at
+// D = 32, is level at D = 64 and 128, and fp32 launches of a few
+// workgroups are 13 % slower with 2.
+constexpr int kLoadsPerTile = FD_LOADS_PER_TILE;
+constexpr int valu_loads_per_tile(int elem_bytes, int dim) {
+  return elem_bytes == 2 && dim <= 32 ? 2 : kLoadsPerTile;
+}
 #ifndef FD_PREFETCH_TILES_VALU
 #define FD_PREFETCH_TILES_VALU 1
 #endif

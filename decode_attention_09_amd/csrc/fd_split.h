@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs 
   constexpr int EPL = 16 / EB;         // elements per 16-byte chunk
   constexpr int LPR = D / EPL;         // lanes per K/V row
   constexpr int RPI = kWave / LPR;     // rows per wave-wide load
-  constexpr int NI = kLoadsPerTile;    // loads per tile (each of K and V)
+  constexpr int NI = valu_loads_per_tile(EB, D);  // loads per tile (each of K and V)
   constexpr int TK = NI * RPI;         // keys per wave tile
   constexpr int NW = kWavesPerGroup;
   static_assert(LPR >= 1 && LPR <= 32 && (NI % 2) == 0, "unsupported geometry");
