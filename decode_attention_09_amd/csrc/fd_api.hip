@@ -207,6 +207,7 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   const int cst = device_cus(&cus);
   if (cst != FD_OK) return cst;
   a.kv_nt = path != FD_PATH_UNPACKED && sz.workgroups >= cus ? 1 : 0;
+  a.wide = sz.workgroups < cus ? 1 : 0;
   dim3 grid((unsigned)sz.workgroups);
   const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;

@@ -8,10 +8,22 @@
 namespace fd {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-#ifndef FD_WAVES_PER_GROUP
-#define FD_WAVES_PER_GROUP 4
+#ifndef FD_WAVES_VALU
+#define FD_WAVES_VALU 4
 #endif
-constexpr int kWavesPerGroup = FD_WAVES_PER_GROUP;  // waves per split workgroup
+#ifndef FD_WAVES_MFMA
+#define FD_WAVES_MFMA 4
+#endif
+// waves per split workgroup of the VALU and the matrix-core kernel
+constexpr int kWavesValu = FD_WAVES_VALU;
+constexpr int kWavesMfma = FD_WAVES_MFMA;
+// VALU workgroups of launches with fewer workgroups than compute units,
+// where each workgroup's own stream sets the time. Measured on MI355X: the
+// fp32 GQA-8 case of 7 workgroups (10,000 keys, D = 128) goes from 82 to
+// 66.5 us with 8 waves; full launches gain nothing (MHA D = 128 level) or
+// lose (D = 16..64 13-43 % slower) with 8, and the matrix-core kernel shows
+// no consistent gain at any launch size.
+constexpr int kWavesValuWide = 8;
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
 constexpr int kLptMaxBatch = 64;   // batches up to this size run longest sequence first
 #ifndef FD_LOADS_PER_TILE
@@ -52,6 +64,7 @@ struct SplitArgs {
   int batch, heads, kv_heads, group, num_splits, row_chunks;
   int rows_per_pass; // query rows of a group per workgroup (<= the kernel's rows)
   int kv_nt;        // 1: K/V loads with the non-temporal cache policy
+  int wide;         // 1: VALU workgroups of kWavesValuWide waves (launches below one pass)
   int direct;       // 1: write out in dtype; 0: write the workspace
   int ceil_bounds;  // 1: ceil-equal split bounds; 0: proportional
   int unnorm;       // 1: workspace holds (m, l, acc); 0: (o_s, lse2_s)

@@ -421,15 +421,14 @@ __device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF 
 }
 
 // --------------------------------------------------------- VALU kernel --
-template <int DT, int D, int GC, bool NT>
-__global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel(SplitArgs a) {
+template <int DT, int D, int GC, bool NT, int NW>
+__global__ __launch_bounds__(kWave* NW) void split_kernel(SplitArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int EPL = 16 / EB;         // elements per 16-byte chunk
   constexpr int LPR = D / EPL;         // lanes per K/V row
   constexpr int RPI = kWave / LPR;     // rows per wave-wide load
   constexpr int NI = valu_loads_per_tile(EB, D);  // loads per tile (each of K and V)
   constexpr int TK = NI * RPI;         // keys per wave tile
-  constexpr int NW = kWavesPerGroup;
   static_assert(LPR >= 1 && LPR <= 32 && (NI % 2) == 0, "unsupported geometry");
 
   const int tid = threadIdx.x;
@@ -638,14 +637,14 @@ __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) 
 }
 
 template <int DT, int GC, bool NT>
-__global__ __launch_bounds__(kWave* kWavesPerGroup) void split_kernel_mfma(SplitArgs a) {
+__global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(SplitArgs a) {
   static_assert(DT == DT_F16 || DT == DT_BF16, "matrix-core path takes 16-bit inputs");
   static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
   constexpr int D = 128;
   constexpr int EB = 2;
   constexpr int TK = 16;           // keys per wave tile
   constexpr int KS = D / 32;       // MFMA k-steps per tile
-  constexpr int NW = kWavesPerGroup;
+  constexpr int NW = kWavesMfma;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -819,9 +818,9 @@ constexpr bool has_mfma_path(int dim) {
 
 template <int DT, int D, bool NT>
 hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
-  dim3 block(kWave * kWavesPerGroup);
   if constexpr (DT != DT_F32 && D == 128) {
     if (mfma) {
+      const dim3 block(kWave * kWavesMfma);
       switch (rows) {
 #define FD_CASE(R) \
   case R: hipLaunchKernelGGL((split_kernel_mfma<DT, R, NT>), grid, block, 0, s, a); break;
@@ -832,9 +831,25 @@ hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, h
       return hipGetLastError();
     }
   }
+  if constexpr (!NT) {  // launches below one pass never take non-temporal loads
+    if (a.wide) {
+      const dim3 block(kWave * kWavesValuWide);
+      switch (rows) {
+#define FD_CASE(R)                                                                            \
+  case R:                                                                                     \
+    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValuWide>), grid, block, 0, s, a); \
+    break;
+        FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
+#undef FD_CASE
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+  }
+  const dim3 block(kWave * kWavesValu);
   switch (rows) {
 #define FD_CASE(R) \
-  case R: hipLaunchKernelGGL((split_kernel<DT, D, R, NT>), grid, block, 0, s, a); break;
+  case R: hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValu>), grid, block, 0, s, a); break;
     FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
 #undef FD_CASE
     default: return hipErrorInvalidValue;
