@@ -25,6 +25,15 @@ constexpr int kWavesMfma = FD_WAVES_MFMA;
 // no consistent gain at any launch size.
 constexpr int kWavesValuWide = 8;
 constexpr int kMaxRowsPerPass = 8; // query rows of one GQA group handled per workgroup
+// Resident matrix-core split workgroups per compute unit, enforced by
+// reserving LDS at launch (registers alone allow 3). Measured on MI355X:
+// the varlen Qwen batch (1024 workgroups of very unequal length) runs its
+// split kernel in 191 instead of 196.5 us, because its longest segments,
+// which end last, get a larger share of the bandwidth; every other matrix-
+// core workload measured is within 0.3 %. Launches the planner sizes to one
+// pass never have more than one workgroup per CU anyway.
+constexpr int kMfmaWorkgroupsPerCu = 2;
+constexpr int kLdsBytesPerCu = 160 * 1024;
 constexpr int kLptMaxBatch = 64;   // batches up to this size run longest sequence first
 #ifndef FD_LOADS_PER_TILE
 #define FD_LOADS_PER_TILE 4

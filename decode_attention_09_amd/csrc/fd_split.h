@@ -816,14 +816,46 @@ constexpr bool has_mfma_path(int dim) {
   return DT != DT_F32 && dim == 128;
 }
 
+// Dynamic LDS that, added to the kernel's static LDS, lets exactly
+// kMfmaWorkgroupsPerCu matrix-core workgroups reside on one compute unit
+// (0 if the device's per-workgroup limit does not allow it). Computed once
+// per kernel instance.
+template <int DT, int GC, bool NT>
+size_t mfma_lds_reserve() {
+  static const size_t bytes = [] {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&split_kernel_mfma<DT, GC, NT>)) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      return (size_t)0;
+    }
+    int dev = 0, max_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess) {
+      (void)hipGetLastError();
+      return (size_t)0;
+    }
+    // per-workgroup total just under kLdsBytesPerCu / k: k fit, k + 1 do not
+    const long total = (long)kLdsBytesPerCu / kMfmaWorkgroupsPerCu - 1024;
+    const long dyn = total - (long)fa.sharedSizeBytes;
+    if (dyn <= 0 || total > (long)max_block) return (size_t)0;
+    return (size_t)dyn;
+  }();
+  return bytes;
+}
+
 template <int DT, int D, bool NT>
 hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
   if constexpr (DT != DT_F32 && D == 128) {
     if (mfma) {
       const dim3 block(kWave * kWavesMfma);
       switch (rows) {
-#define FD_CASE(R) \
-  case R: hipLaunchKernelGGL((split_kernel_mfma<DT, R, NT>), grid, block, 0, s, a); break;
+#define FD_CASE(R)                                                                        \
+  case R:                                                                                 \
+    hipLaunchKernelGGL((split_kernel_mfma<DT, R, NT>), grid, block,                       \
+                       (mfma_lds_reserve<DT, R, NT>()), s, a);                            \
+    break;
         FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
 #undef FD_CASE
         default: return hipErrorInvalidValue;
