@@ -261,8 +261,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mha_b4_h32_l4096_d128_f16")
-    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--all", action="store_true",
+                    help="one line per workload (no CPU leg unless --cpu-seconds is given)")
+    ap.add_argument("--cpu-seconds", type=float, default=None,
+                    help="oracle time budget per CPU leg (default 10 for one workload, "
+                         "0 = no CPU leg for --all and --sweep-splits)")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="override the workload's split count (sweeps)")
     ap.add_argument("--kernel-path", choices=["auto", "valu", "mfma", "unpacked"],
@@ -300,14 +303,16 @@ def main():
             splits = [int(x) for x in args.sweep_splits.split(",") if x]
             todo = [(workload_by_name(n), ns) for n in args.workload.split(",")
                     for ns in splits]
+        cpu_s = args.cpu_seconds or 0.0
         for w, ns in todo:
-            r = run(w, args.steps, args.warmup, 0.0, ns_override=ns, rows_per_workgroup=rows,
+            r = run(w, args.steps, args.warmup, cpu_s, ns_override=ns, rows_per_workgroup=rows,
                     fmt=args.format)
             r["kernel_path"] = args.kernel_path
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
         return
-    r = run(workload_by_name(args.workload), args.steps, args.warmup, args.cpu_seconds,
+    cpu_s = 10.0 if args.cpu_seconds is None else args.cpu_seconds
+    r = run(workload_by_name(args.workload), args.steps, args.warmup, cpu_s,
             ns_override=args.num_splits, rows_per_workgroup=rows, fmt=args.format)
     r["kernel_path"] = args.kernel_path
     print(json.dumps(r), flush=True)
