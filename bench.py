@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -37,11 +38,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["fd_split.h", "fd_internal.h"]
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace (string literals in these
+    kernel sources hold no comment markers), so edits to comments alone do
+    not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for n in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_09_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "decode_attention_09_amd", "csrc", n)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,7 +34,8 @@
 //    size ends at the last valid row of the segment, so rows past the
 //    segment (or the tensor) read as zero without branches, and are then
 //    masked out of the softmax.
-//  * Four waves per workgroup take interleaved tiles of the segment and are
+//  * The waves of a workgroup (4; 8 for VALU launches with fewer workgroups
+//    than compute units) take interleaved tiles of the segment and are
 //    merged through LDS at the end (the same LSE merge as the combine).
 //  * Register tile pipeline: the loads of the next kPrefetchTilesValu
 //    (kPrefetchTilesMfma) tiles are in flight while the current tile is
