@@ -1,0 +1,69 @@
+"""Host logic of bench.py (no GPU): the single-GPU guard, the kernel-source
+hash that keys the committed HBM traffic counters, the committed counters
+themselves, and the workgroup count it reports."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single" in r.stderr
+    assert r.stdout == ""
+
+
+def test_code_hash_ignores_comments_and_whitespace():
+    a = "int f(int x) {  // doubles x\n  return 2 * x; /* no\n overflow check */ }\n"
+    b = "int f(int x) {\n    return 2 * x;   // other words\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_kernel_hash_is_stable_and_short():
+    h = bench.kernel_hash()
+    assert h == bench.kernel_hash()
+    assert len(h) == 16 and all(ch in "0123456789abcdef" for ch in h)
+
+
+def test_committed_traffic_counters_are_plausible():
+    """Every committed entry: HBM bytes per split launch between the
+    algorithmic K/V bytes (each byte read once) and 10 % above them (the
+    partials, q and the counters' rounding), for a workload bench.py knows."""
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    names = {w.name for w in W.all_workloads()}
+    assert t, "no committed traffic counters"
+    for name, e in t.items():
+        assert name in names
+        ratio = e["hbm_bytes_per_launch"] / e["algorithmic_bytes_per_launch"]
+        assert 0.99 <= ratio <= 1.10, (name, ratio)
+        assert abs(e["fetch_scale"] - 0.5) < 0.05 and abs(e["write_scale"] - 1.0) < 0.05
+
+
+def test_traffic_is_reported_only_for_the_current_kernel():
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    for name, e in t.items():
+        got = bench.traffic_for(name)
+        if e["kernel_hash"] == bench.kernel_hash():
+            assert got == e["hbm_bytes_per_launch"]
+        else:
+            assert got is None
+    assert bench.traffic_for("no_such_workload") is None
+
+
+def test_split_workgroups_counts_row_chunks_and_splits():
+    llama = W.llama(16, 8192)             # 8 KV heads, group 4
+    assert bench.split_workgroups(llama, 2, 8) == 16 * 8 * 1 * 2
+    assert bench.split_workgroups(llama, 2, 1) == 16 * 8 * 4 * 2   # unpacked: one row each
+    varlen = W.varlen_qwen()              # 4 KV heads, group 7
+    assert bench.split_workgroups(varlen, 8, 8) == 32 * 4 * 8
