@@ -171,6 +171,34 @@ def test_nan_outside_sequences_is_never_read(layout, kernel_path):
         assert H.max_err(out, ref) <= H.TOL["f16"]
 
 
+def test_offsets_need_not_start_at_zero(kernel_path):
+    """cu_seqlens_k is any non-decreasing offset array: here it starts at 37
+    and holds an empty sequence, and every K/V row outside the sequences is
+    NaN, so a read of one would show in the output."""
+    lengths = [300, 0, 1000, 17]
+    base = _rand_inputs(lengths, 16, 2, 128, "f16", seed=5)
+    off, pad, T = 37, 16, sum(lengths)
+    k = torch.full((off + T + pad, 2, 128), float("nan"), dtype=base.k.dtype, device=H.DEV)
+    v = torch.full_like(k, float("nan"))
+    k[off:off + T] = base.k[:T]
+    v[off:off + T] = base.v[:T]
+    cu = (base.cu_seqlens_k + off).contiguous()
+    inp = W.Inputs(base.workload, base.q, k, v, cu, lengths)
+    cu_h = cu.cpu().tolist()
+    assert cu_h[0] == off
+    for ns in (1, 3):
+        out = H.host(H.gpu_attention(inp, ns))
+        assert np.isfinite(out).all()
+        assert not out[1].any()
+        for b in (0, 2, 3):
+            for j in range(2):
+                ref = oracle.attention_rows(H.host(base.q[b, 8 * j:8 * (j + 1)]),
+                                            H.host(k[cu_h[b]:cu_h[b + 1], j]),
+                                            H.host(v[cu_h[b]:cu_h[b + 1], j]), 1.0 / math.sqrt(128))
+                err = H.max_err(out[b, 8 * j:8 * (j + 1)], ref)
+                assert err <= H.TOL["f16"], (ns, b, j, err)
+
+
 @pytest.mark.parametrize("group,kv_heads", [(16, 2), (64, 1), (9, 3), (12, 1)])
 @pytest.mark.parametrize("dim", [64, 128])
 def test_groups_larger_than_one_pass(group, kv_heads, dim, kernel_path):
