@@ -142,7 +142,9 @@ def kv_layout(k, layout: str = "packed"):
     """Strides (elements) of a K or V tensor for the C ABI.
 
     "packed": k is [total_kv, kv_heads, dim]; "bhsd": k is
-    [batch, kv_heads, max_len, dim]. The last dim must be contiguous.
+    [batch, kv_heads, max_len, dim]; "bshd": k is [batch, max_len, kv_heads,
+    dim]. Views are fine (the tensor's own strides are used); the last dim
+    must be contiguous.
     """
     if k.stride(-1) != 1:
         raise ValueError("the head dim of K/V must be contiguous")
@@ -154,6 +156,10 @@ def kv_layout(k, layout: str = "packed"):
         if k.dim() != 4:
             raise ValueError("bhsd K/V must be [batch, kv_heads, max_len, dim]")
         return FdKvLayout(k.stride(0), k.stride(1), k.stride(2), 0)
+    if layout == "bshd":
+        if k.dim() != 4:
+            raise ValueError("bshd K/V must be [batch, max_len, kv_heads, dim]")
+        return FdKvLayout(k.stride(0), k.stride(2), k.stride(1), 0)
     raise ValueError(f"unknown layout {layout!r}")
 
 
@@ -176,16 +182,42 @@ def fd_workspace_bytes_unnorm(batch: int, heads: int, dim: int, num_splits: int)
     return int(load_library().fd_workspace_bytes_unnorm(batch, heads, dim, num_splits))
 
 
-def _sizes(q, k, cu):
+# Axis of the KV-head index in K/V, per layout name of kv_layout.
+_KV_HEAD_AXIS = {"packed": 1, "bhsd": 1, "bshd": 2}
+
+
+def _sizes(q, k, v, cu, layout):
+    """Sizes for the C call, after checking that q, k, v and cu agree: the C
+    ABI applies one stride set to K and V and reads everything on one
+    device, so mismatches are refused here rather than misread there."""
+    import torch
     if q.dim() != 3:
         raise ValueError("q must be [batch, heads, dim]")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
+    if layout not in _KV_HEAD_AXIS:
+        raise ValueError(f"unknown layout {layout!r}")
     batch, heads, dim = q.shape
-    kv_heads = k.shape[1]
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must have the same dtype")
+    if k.shape[-1] != dim:
+        raise ValueError("the head dim of K/V must equal that of q")
+    if not (q.device == k.device == v.device == cu.device):
+        raise ValueError("q, k, v and cu_seqlens_k must be on one device")
+    if cu.dtype != torch.int32 or not cu.is_contiguous():
+        raise TypeError("cu_seqlens_k must be a contiguous int32 tensor")
+    kv_heads = k.shape[_KV_HEAD_AXIS[layout]]
     if cu.numel() != batch + 1:
         raise ValueError("cu_seqlens_k must have batch + 1 entries")
     return batch, heads, kv_heads, dim
+
+
+def _check_out(out, q):
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q ([batch, heads, dim], same dtype)")
 
 
 def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
@@ -202,11 +234,12 @@ def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
 def _attention(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, out, workspace, layout,
                stream):
     import torch
-    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
+    batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q)
     if num_splits > 1:
         workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
     lay = kv_layout(k, layout)
@@ -218,7 +251,7 @@ def _attention(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, out, work
 
 
 def _split(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, workspace, layout, stream):
-    batch, heads, kv_heads, dim = _sizes(q, k, cu_seqlens_k)
+    batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
     workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
@@ -231,6 +264,13 @@ def _split(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, workspace, la
 
 
 def _combine(name, workspace, batch, heads, dim, num_splits, out, stream):
+    if tuple(out.shape) != (batch, heads, dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [batch, heads, dim] tensor")
+    size = fd_workspace_bytes_unnorm if name.endswith("_unnorm") else fd_workspace_bytes
+    if workspace.numel() * workspace.element_size() < size(batch, heads, dim, num_splits):
+        raise ValueError("workspace smaller than the split launch wrote")
+    if workspace.device != out.device:
+        raise ValueError("workspace and out must be on one device")
     _check(getattr(load_library(), name)(
         _ptr(workspace), batch, heads, dim, int(num_splits), _ptr(out),
         _stream(stream, out.device), _dtype_code(out)), name)

@@ -231,3 +231,74 @@ def test_kernel_path_setting():
     assert _lib().fd_set_kernel_path(7) == -1
     with pytest.raises(ValueError):
         fd.fd_set_kernel_path(9)
+
+
+# ------------------------------------------- binding argument marshalling --
+def _cpu_inputs(B=2, H=8, Hkv=2, D=64, T=40):
+    import torch
+    q = torch.zeros(B, H, D, dtype=torch.float16)
+    k = torch.zeros(T, Hkv, D, dtype=torch.float16)
+    v = torch.zeros(T, Hkv, D, dtype=torch.float16)
+    cu = torch.tensor([0, 10, T], dtype=torch.int32)
+    return q, k, v, cu
+
+
+def test_binding_refuses_mismatched_tensors_before_any_call():
+    """The C ABI applies one stride set to K and V and reads one device: the
+    binding refuses inputs that disagree before calling into the library."""
+    import torch
+    q, k, v, cu = _cpu_inputs()
+    cases = [
+        dict(v=torch.zeros(40, 2, 64, dtype=torch.float16).transpose(0, 1).contiguous()
+             .transpose(0, 1)),                                     # other strides
+        dict(v=torch.zeros(41, 2, 64, dtype=torch.float16)),        # other shape
+        dict(k=k.float(), v=v.float()),                             # dtype differs from q
+        dict(k=torch.zeros(40, 2, 32, dtype=torch.float16),
+             v=torch.zeros(40, 2, 32, dtype=torch.float16)),        # head dim differs
+        dict(cu=cu.long()),                                         # not int32
+        dict(cu=torch.tensor([0, 40], dtype=torch.int32)),          # not batch + 1 entries
+        dict(q=q.transpose(0, 1)),                                  # q not contiguous
+    ]
+    for c in cases:
+        a = dict(q=q, k=k, v=v, cu=cu)
+        a.update(c)
+        with pytest.raises((ValueError, TypeError)):
+            fd.fd_decode_attention(a["q"], a["k"], a["v"], a["cu"], 2)
+        with pytest.raises((ValueError, TypeError)):
+            fd.fd_decode_split(a["q"], a["k"], a["v"], a["cu"], 2)
+    with pytest.raises(ValueError):
+        fd.fd_decode_attention(q, k, v, cu, 2, out=torch.zeros(2, 8, 32, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        fd.fd_decode_attention(q, k, v, cu, 2, layout="hbsd")
+
+
+def test_binding_refuses_a_short_workspace_or_wrong_out_in_combine():
+    import torch
+    out = torch.zeros(2, 8, 64, dtype=torch.float16)
+    need = fd.fd_workspace_bytes(2, 8, 64, 3)
+    with pytest.raises(ValueError):
+        fd.fd_decode_combine(torch.zeros(need - 1, dtype=torch.uint8), 2, 8, 64, 3, out)
+    with pytest.raises(ValueError):
+        fd.fd_decode_combine(torch.zeros(need, dtype=torch.uint8), 2, 8, 128, 3, out)
+
+
+def test_kv_layout_strides():
+    """Element strides handed to the C ABI for each layout name; row
+    (b, t, j) starts at b*batch + cu[b]*cu + t*token + j*head."""
+    import torch
+    packed = torch.zeros(100, 4, 64)
+    lay = fd.kv_layout(packed, "packed")
+    assert (lay.batch_stride, lay.head_stride, lay.token_stride, lay.cu_stride) == (0, 64, 256, 256)
+    bhsd = torch.zeros(3, 4, 50, 64)
+    lay = fd.kv_layout(bhsd, "bhsd")
+    assert (lay.batch_stride, lay.head_stride, lay.token_stride, lay.cu_stride) == (
+        4 * 50 * 64, 50 * 64, 64, 0)
+    bshd = torch.zeros(3, 50, 4, 64)
+    lay = fd.kv_layout(bshd, "bshd")
+    assert (lay.batch_stride, lay.head_stride, lay.token_stride, lay.cu_stride) == (
+        50 * 4 * 64, 64, 4 * 64, 0)
+    view = torch.zeros(3, 4, 80, 64)[:, :, :50]          # a cache with spare capacity
+    lay = fd.kv_layout(view, "bhsd")
+    assert (lay.batch_stride, lay.head_stride, lay.token_stride) == (4 * 80 * 64, 80 * 64, 64)
+    with pytest.raises(ValueError):
+        fd.kv_layout(torch.zeros(3, 4, 64, 50).transpose(2, 3), "bhsd")

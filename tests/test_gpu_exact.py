@@ -171,6 +171,22 @@ def test_nan_outside_sequences_is_never_read(layout, kernel_path):
         assert H.max_err(out, ref) <= H.TOL["f16"]
 
 
+def test_bshd_layout_matches_bhsd_bitwise(kernel_path):
+    """[batch, max_len, kv_heads, dim] K/V (kv_layout "bshd") reads the same
+    values in the same order as [batch, kv_heads, max_len, dim], so the
+    outputs are bitwise equal; the latter is checked against the oracle."""
+    inp = _rand_inputs([300, 77, 1000], 16, 2, 128, "f16", layout="bhsd", seed=9)
+    k_s = inp.k.transpose(1, 2).contiguous()
+    v_s = inp.v.transpose(1, 2).contiguous()
+    fdm = H.fd()
+    for ns in (1, 4):
+        a = fdm.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns, layout="bhsd")
+        b = fdm.fd_decode_attention(inp.q, k_s, v_s, inp.cu_seqlens_k, ns, layout="bshd")
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), ns
+        assert H.max_err(H.host(a), H.oracle_full(inp, ns)) <= H.TOL["f16"]
+
+
 def test_offsets_need_not_start_at_zero(kernel_path):
     """cu_seqlens_k is any non-decreasing offset array: here it starts at 37
     and holds an empty sequence, and every K/V row outside the sequences is
