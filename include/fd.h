@@ -79,10 +79,15 @@ enum {
  * shape_kv):        {0, dim, kv_heads*dim, kv_heads*dim}
  * Padded [batch, kv_heads, max_len, dim] (flash_decode_splitk.py's
  * [batch, heads, seqlen, dim]): {kv_heads*max_len*dim, max_len*dim, dim, 0}
+ * Padded [batch, max_len, kv_heads, dim]:
+ *                   {max_len*kv_heads*dim, dim, kv_heads*dim, 0}
+ * (a view into a larger cache uses that cache's strides).
  *
  * Field order: batch_stride, head_stride, token_stride, cu_stride. All are
- * >= 0, token_stride >= dim, and stride*element_size must be a multiple of
- * 16 bytes. K and V share the layout. NULL means packed.
+ * >= 0, token_stride >= dim, every stride*element_size is a multiple of 16
+ * bytes, and token_stride*element_size <= 8 MiB (offsets inside one tile of
+ * keys are 32-bit); otherwise FD_ERR_INVALID_ARG. K and V share the layout.
+ * NULL means packed.
  */
 typedef struct fd_kv_layout {
   int64_t batch_stride;
