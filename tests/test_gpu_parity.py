@@ -2,7 +2,6 @@
 seeded workloads of the pages, at the stated max-abs tolerances (fp32 1e-5,
 fp16 2e-3, bf16 1e-2), plus the pages' own cases."""
 import json
-import math
 import os
 
 import numpy as np

@@ -5,7 +5,6 @@ below the split count included), split count, K/V layout (packed,
 every output row against the fp64 oracle's direct attention at the dtype's
 tolerance (empty sequences: zero rows). K/V rows outside the sequences are
 NaN, so an over-read shows."""
-import math
 
 import numpy as np
 import pytest

@@ -9,7 +9,6 @@ the quantities it defines: m_s and m_s + log2 l_s (the split's base-2 LSE)
 within 1e-4 -- the fp32 rounding of base-2 scores of magnitude <= ~10 summed
 over <= 128 products -- and acc_s / l_s and the merged output within the
 dtype tolerances (fp32 1e-5, fp16 2e-3, bf16 1e-2)."""
-import math
 
 import numpy as np
 import pytest
