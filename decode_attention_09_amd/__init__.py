@@ -231,10 +231,23 @@ def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
     return workspace
 
 
+def _plan_from_device_lengths(q, cu, heads, kv_heads, dim) -> int:
+    """fd_plan_splits on the lengths in cu_seqlens_k (copied to the host,
+    which waits for the device). Empty sequences are left out of the plan:
+    the kernels write zero rows for them under any split count."""
+    lens = (cu[1:] - cu[:-1]).tolist()
+    live = [L for L in lens if L > 0]
+    if not live:
+        return 1
+    return fd_plan_splits(len(live), heads, kv_heads, dim, _dtype_code(q), live)
+
+
 def _attention(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, out, workspace, layout,
                stream):
     import torch
     batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
+    if num_splits is None:
+        num_splits = _plan_from_device_lengths(q, cu_seqlens_k, heads, kv_heads, dim)
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
     if out is None:
@@ -277,9 +290,13 @@ def _combine(name, workspace, batch, heads, dim, num_splits, out, stream):
     return out
 
 
-def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int, scale: float | None = None,
+def fd_decode_attention(q, k, v, cu_seqlens_k, num_splits: int | None, scale: float | None = None,
                         out=None, workspace=None, layout: str = "packed", stream=None):
-    """out[b,h] = softmax(scale q[b,h].K_b^T) V_b through libfd's two launches."""
+    """out[b,h] = softmax(scale q[b,h].K_b^T) V_b through libfd's two launches.
+
+    num_splits=None asks fd_plan_splits for the count, on the lengths in
+    cu_seqlens_k; reading them to the host waits for the device, so pass the
+    count (planned once from host-side lengths) where that matters."""
     return _attention("fd_decode_attention", False, q, k, v, cu_seqlens_k, num_splits, scale,
                       out, workspace, layout, stream)
 
@@ -297,10 +314,11 @@ def fd_decode_combine(workspace, batch: int, heads: int, dim: int, num_splits: i
     return _combine("fd_decode_combine", workspace, batch, heads, dim, num_splits, out, stream)
 
 
-def fd_decode_attention_unnorm(q, k, v, cu_seqlens_k, num_splits: int,
+def fd_decode_attention_unnorm(q, k, v, cu_seqlens_k, num_splits: int | None,
                                scale: float | None = None, out=None, workspace=None,
                                layout: str = "packed", stream=None):
-    """The same attention with ceil-equal bounds and (m, l, acc) partials."""
+    """The same attention with ceil-equal bounds and (m, l, acc) partials
+    (num_splits=None: as in fd_decode_attention)."""
     return _attention("fd_decode_attention_unnorm", True, q, k, v, cu_seqlens_k, num_splits,
                       scale, out, workspace, layout, stream)
 

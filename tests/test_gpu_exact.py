@@ -187,6 +187,23 @@ def test_bshd_layout_matches_bhsd_bitwise(kernel_path):
         assert H.max_err(H.host(a), H.oracle_full(inp, ns)) <= H.TOL["f16"]
 
 
+def test_planned_split_count_when_none_is_given():
+    """num_splits=None plans on the device lengths (empty sequences left
+    out) and gives the same output as passing that count explicitly."""
+    fdm = H.fd()
+    inp = _rand_inputs([5000, 0, 1200, 64], 32, 8, 128, "bf16", seed=13)
+    live = [L for L in inp.lengths if L > 0]
+    ns = fdm.fd_plan_splits(len(live), 32, 8, 128, fdm.FD_BF16, live)
+    a = fdm.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, None)
+    b = fdm.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    u = fdm.fd_decode_attention_unnorm(inp.q, inp.k, inp.v, inp.cu_seqlens_k, None)
+    torch.cuda.synchronize()
+    assert H.max_err(H.host(u), H.host(b)) <= H.TOL["bf16"]
+    assert not H.host(a)[1].any()
+
+
 def test_offsets_need_not_start_at_zero(kernel_path):
     """cu_seqlens_k is any non-decreasing offset array: here it starts at 37
     and holds an empty sequence, and every K/V row outside the sequences is
