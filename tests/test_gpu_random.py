@@ -1,10 +1,20 @@
 """Seeded random sweep over the whole call: each case draws dtype, head dim,
 group size, KV heads, batch, ragged lengths (empty sequences and lengths
 below the split count included), split count, K/V layout (packed,
-[B, Hkv, S, D], [B, S, Hkv, D]), split format and kernel path, and checks
-every output row against the fp64 oracle's direct attention at the dtype's
-tolerance (empty sequences: zero rows). K/V rows outside the sequences are
-NaN, so an over-read shows."""
+[B, Hkv, S, D], [B, S, Hkv, D]), split format, kernel path and sometimes a
+non-default scale, and checks every output element against the fp64
+oracle's direct attention (empty sequences: zero rows). K/V rows outside
+the sequences are NaN, so an over-read shows.
+
+Bound: the dtype's max-abs tolerance plus one unit in the last place of the
+output dtype at the reference's magnitude. The output is written in the
+input dtype, as the pages' reference casts it; with scales up to 16x the
+default the softmax collapses onto a few keys and |o| approaches the
+largest |v| (about 4), where one bf16 ulp is 0.016 -- so the final cast of
+even the exact result can miss a fixed 1e-2, and any result computed in
+fp32 can land one ulp away from the rounded exact value. At the default
+scale (all the workload tests) outputs stay far below 1 and the fixed
+tolerances apply unchanged."""
 
 import numpy as np
 import pytest
@@ -18,6 +28,14 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 120
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "unpacked": 3}
+MANTISSA_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the output dtype at |x| (normal range; the smallest normal
+    exponent is a floor for tiny values)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(ax)) - MANTISSA_BITS[dtype])
 
 
 def _draw(i: int):
@@ -97,5 +115,5 @@ def test_random_case_matches_oracle(c):
             kr = oracle.kv_rows(kh, cu, b, j, base_layout)
             vr = oracle.kv_rows(vh, cu, b, j, base_layout)
             ref = oracle.attention_rows(q[b, j * G:(j + 1) * G], kr, vr, scale)
-            err = H.max_err(rows, ref)
-            assert err <= H.TOL[c["dtype"]], (b, j, L, err)
+            excess = np.abs(rows - ref) - (H.TOL[c["dtype"]] + ulp(ref, c["dtype"]))
+            assert excess.max() <= 0.0, (b, j, L, H.max_err(rows, ref), excess.max())
