@@ -16,6 +16,12 @@ workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
     python bench.py --workload NAME[,NAME...] --sweep-splits 1,2,4,8 [--kernel-path P]
+    python bench.py --all --graph     # timed calls replayed from one captured HIP graph
+
+Eager timing (the default) issues every call from Python; through the binding
+that costs the host ~12 us per call, which bounds the smallest shapes
+(<= ~12 us of GPU work per call). --graph captures the timed calls once and
+replays them, so those shapes show their GPU time.
 """
 from __future__ import annotations
 
@@ -145,7 +151,7 @@ def split_workgroups(w, ns: int, rows_per_workgroup: int) -> int:
 
 
 def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES,
-        ns_override: int = 0, rows_per_workgroup: int = 8, fmt: str = "lse"):
+        ns_override: int = 0, rows_per_workgroup: int = 8, fmt: str = "lse", graph: bool = False):
     import torch
     import workloads as W
     import decode_attention_09_amd as fd
@@ -168,23 +174,45 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     attention = fd.fd_decode_attention_unnorm if unnorm else fd.fd_decode_attention
     split = fd.fd_decode_split_unnorm if unnorm else fd.fd_decode_split
 
-    def step(i):
+    def step(i, s=None):
         k, v = ks[i % copies], vs[i % copies]
         attention(inp.q, k, v, inp.cu_seqlens_k, ns, out=out, workspace=ws, layout=w.layout,
-                  stream=stream)
+                  stream=stream if s is None else s)
 
-    def split_only(i):
+    def split_only(i, s=None):
         k, v = ks[i % copies], vs[i % copies]
-        split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout, stream=stream)
+        split(inp.q, k, v, inp.cu_seqlens_k, ns, workspace=ws, layout=w.layout,
+              stream=stream if s is None else s)
 
     def timed(fn, n, offset):
+        """Mean ms per call of n back-to-back calls: issued one by one from
+        Python (eager), or captured once in a HIP graph and replayed (graph),
+        which takes the host's issue cost (~12 us per call through the
+        binding) out of the measurement."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        g = None
+        if graph:
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                fn(offset, side)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream()
+                for i in range(n):
+                    fn(offset + i, cs)
+            g.replay()                  # first replay untimed
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
-        for i in range(n):
-            fn(offset + i)
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(n):
+                fn(offset + i)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n, time.perf_counter() - t0
@@ -243,6 +271,7 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
                      "kernel_us": round(split_avg * 1e3, 3),
                      "algorithmic_bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
+        "timing": "graph replay" if graph else "eager calls",
     }
     if cpu_s > 0:
         res["cpu_baseline"] = cpu_baseline(inp, ns, cpu_s, fmt)
@@ -288,6 +317,9 @@ def main():
     ap.add_argument("--sweep-splits", default="",
                     help="comma-separated split counts: one line (no CPU leg) per "
                          "workload in --workload (comma-separated) and split count")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the calls as one captured HIP graph replay instead of eager "
+                         "calls (takes the host's per-call issue cost out; for small shapes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 10 times (reference for the "
                          "FETCH_SIZE/WRITE_SIZE counters)")
@@ -316,14 +348,15 @@ def main():
         cpu_s = args.cpu_seconds or 0.0
         for w, ns in todo:
             r = run(w, args.steps, args.warmup, cpu_s, ns_override=ns, rows_per_workgroup=rows,
-                    fmt=args.format)
+                    fmt=args.format, graph=args.graph)
             r["kernel_path"] = args.kernel_path
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
         return
     cpu_s = 10.0 if args.cpu_seconds is None else args.cpu_seconds
     r = run(workload_by_name(args.workload), args.steps, args.warmup, cpu_s,
-            ns_override=args.num_splits, rows_per_workgroup=rows, fmt=args.format)
+            ns_override=args.num_splits, rows_per_workgroup=rows, fmt=args.format,
+            graph=args.graph)
     r["kernel_path"] = args.kernel_path
     print(json.dumps(r), flush=True)
 
