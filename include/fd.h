@@ -31,10 +31,15 @@
  *   - All tensor pointers are device pointers, owned by the caller, and must
  *     be 16-byte aligned. The library allocates no device memory and keeps
  *     no per-call state; calls are asynchronous on `stream` (a hipStream_t
- *     passed as void*, NULL = the default stream) and never synchronise.
+ *     passed as void*, NULL = the default stream), never synchronise and
+ *     record no memset, so they can be captured in a HIP graph. The first
+ *     call of a configuration on a device queries device and kernel
+ *     attributes (cached afterwards): make it outside the capture.
  *   - Element type `dtype` (FD_F32, FD_F16, FD_BF16) applies to q, k, v and
- *     out. Arithmetic is fp32 throughout; out is rounded to dtype
- *     (round-to-nearest-even).
+ *     out. Scores, the softmax statistics and all accumulation are fp32;
+ *     for fp16/bf16 the probabilities are rounded to dtype (round to
+ *     nearest even) for the P.V products, which accumulate in fp32; out is
+ *     rounded to dtype (round-to-nearest-even).
  *   - Return value: FD_OK or an FD_ERR_* code. Argument checks run on the
  *     host before anything is launched; a failed check launches nothing and
  *     leaves every buffer untouched.
