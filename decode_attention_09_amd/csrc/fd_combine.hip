@@ -5,7 +5,8 @@
 
 namespace fd {
 
-// The merge of one (sequence, head) by a workgroup of NWAVES waves.
+// The merge of one (sequence, head), or of D of its dims, by a workgroup of
+// NWAVES waves.
 //
 // Normalised format (UNNORM = false), the combine segment of
 // gqa_decode_splitkv in "decode_attention_splitkv.py" (TileLang tutorial,
@@ -21,7 +22,7 @@ namespace fd {
 // (every key -inf) is written as zeros.
 //
 // key[s * kst] is lse_s or m_s, lw[s * kst] is l_s (unnormalised format),
-// op[s * D + d] the partial row of split s. Each wave owns a strided subset
+// op[s * RS + d] the partial row of split s (RS: the head dim). Each wave owns a strided subset
 // of the partial rows (SPW rows side by side, D/64 dims per lane when
 // D >= 64). Every load the merge needs is issued up front -- one key (and l)
 // per thread for the max and the sum, and the first KR partial rows of each
@@ -29,15 +30,17 @@ namespace fd {
 // beyond KR (many splits) are read after the reductions. The waves' maxima,
 // sums and row sums meet in LDS. All threads of the workgroup must call it
 // (it synchronises).
-template <int DT, int D, int NWAVES, bool UNNORM>
+template <int DT, int D, int NWAVES, bool UNNORM, int RS = D, int KR = 8>
 __device__ __forceinline__ void combine_head(const float* op, const float* key, const float* lw,
-                                             int64_t kst, int ns, void* out, int64_t bh) {
+                                             int64_t kst, int ns, void* out, int64_t obase) {
+  // D: dims this workgroup merges; RS: row stride of the partials (the head
+  // dim); KR: rows per lane group held in registers; out + obase: the
+  // first output element of those D dims.
   constexpr int NT = kWave * NWAVES;
   constexpr int DPL = D >= kWave ? D / kWave : 1;  // dims per lane
   constexpr int LPS = D / DPL;                     // lanes per partial row
   constexpr int SPW = kWave / LPS;                 // rows a wave reads side by side
   constexpr int RPG = SPW * NWAVES;                // rows the group reads side by side
-  constexpr int KR = 8;                            // rows per lane group held in registers
   __shared__ float red[NWAVES];
   __shared__ float part[NWAVES][D];
 
@@ -58,7 +61,7 @@ __device__ __forceinline__ void combine_head(const float* op, const float* key, 
     const bool in = s < ns;
     pk[k] = in ? key[(int64_t)s * kst] : kNegInf;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) pv[k][e] = in ? op[(int64_t)s * D + dl * DPL + e] : 0.0f;
+    for (int e = 0; e < DPL; ++e) pv[k][e] = in ? op[(int64_t)s * RS + dl * DPL + e] : 0.0f;
   }
 
   float mx = k_own;
@@ -110,7 +113,7 @@ __device__ __forceinline__ void combine_head(const float* op, const float* key, 
         wt[u] = weight(key[(int64_t)(s + u * RPG) * kst]);
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
-          v[u][e] = op[(int64_t)(s + u * RPG) * D + dl * DPL + e];
+          v[u][e] = op[(int64_t)(s + u * RPG) * RS + dl * DPL + e];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -121,7 +124,7 @@ __device__ __forceinline__ void combine_head(const float* op, const float* key, 
       const float wt = weight(key[(int64_t)s * kst]);
 #pragma unroll
       for (int e = 0; e < DPL; ++e)
-        acc[e] = __builtin_fmaf(wt, op[(int64_t)s * D + dl * DPL + e], acc[e]);
+        acc[e] = __builtin_fmaf(wt, op[(int64_t)s * RS + dl * DPL + e], acc[e]);
     }
   }
 #pragma unroll
@@ -135,35 +138,59 @@ __device__ __forceinline__ void combine_head(const float* op, const float* key, 
     float o = part[0][d];
 #pragma unroll
     for (int w = 1; w < NWAVES; ++w) o += part[w][d];
-    store_out<DT>(out, bh * D + d, o);
+    store_out<DT>(out, obase + d, o);
   }
 }
 
 constexpr int kCombineWaves = 4;
 
-// One workgroup of four waves per (sequence, head).
-template <int DT, int D>
+// One workgroup of four waves per (sequence, head) and chunk of C of the
+// head's D dims (C = 1: the whole head).
+template <int DT, int D, int C, int KR>
 __global__ __launch_bounds__(kWave* kCombineWaves) void combine_kernel(CombineArgs a) {
-  const int64_t bh = blockIdx.x;
+  constexpr int DC = D / C;
+  const int64_t bh = blockIdx.x / C;
+  const int c = (int)(blockIdx.x % C);
   const int ns = a.num_splits;
-  const float* op = a.opart + bh * ns * D;
+  const float* op = a.opart + bh * ns * D + c * DC;
+  const int64_t obase = bh * D + c * DC;
   if (a.unnorm) {
     // m_s, l_s at [B, H, ns]
-    combine_head<DT, D, kCombineWaves, true>(op, a.mbuf + bh * ns, a.lbuf + bh * ns, 1, ns,
-                                             a.out, bh);
+    combine_head<DT, DC, kCombineWaves, true, D, KR>(op, a.mbuf + bh * ns, a.lbuf + bh * ns, 1,
+                                                     ns, a.out, obase);
   } else {
     // lse_s at [B, ns, H]: split stride = heads
     const int64_t b = bh / a.heads, h = bh % a.heads;
-    combine_head<DT, D, kCombineWaves, false>(op, a.lse + b * ns * a.heads + h, nullptr,
-                                              a.heads, ns, a.out, bh);
+    combine_head<DT, DC, kCombineWaves, false, D, KR>(op, a.lse + b * ns * a.heads + h, nullptr,
+                                                      a.heads, ns, a.out, obase);
   }
 }
 
+// Few (sequence, head) pairs with many splits leave most compute units idle
+// and each workgroup reading its rows in several dependent rounds; then
+// four workgroups share a head, 32 dims each, with every partial row loaded
+// before the reductions. Measured on MI355X, per call: flash-decoding
+// B1/64K (16 heads, 128 splits) 21.1 -> 19.2 us, B1/128K 31.8 -> 29.8 us,
+// B2/32K (64 splits) 20.3 -> 19.6 us, Llama B1/64K at 128 splits
+// 51.9 -> 49.8 us; at 32 splits or fewer, or more heads, no difference.
+#ifndef FD_COMBINE_CHUNK_HEADS
+#define FD_COMBINE_CHUNK_HEADS 64
+#endif
+#ifndef FD_COMBINE_CHUNK_MIN_SPLITS
+#define FD_COMBINE_CHUNK_MIN_SPLITS 33
+#endif
+
 template <int DT, int D>
 static void launch_combine_d(const CombineArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.batch * a.heads));
-  dim3 block(kWave * kCombineWaves);
-  hipLaunchKernelGGL((combine_kernel<DT, D>), grid, block, 0, s, a);
+  const dim3 block(kWave * kCombineWaves);
+  const int64_t bh = (int64_t)a.batch * a.heads;
+  if constexpr (D == 128) {
+    if (bh <= FD_COMBINE_CHUNK_HEADS && a.num_splits >= FD_COMBINE_CHUNK_MIN_SPLITS) {
+      hipLaunchKernelGGL((combine_kernel<DT, D, 4, 16>), dim3((unsigned)(bh * 4)), block, 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((combine_kernel<DT, D, 1, 8>), dim3((unsigned)bh), block, 0, s, a);
 }
 
 template <int DT>
