@@ -272,6 +272,33 @@ def test_runs_on_a_side_stream():
     assert torch.equal(out, ref)
 
 
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no per-call state: calls issued alternately on two
+    streams (each with its own workspace and output, different inputs and
+    kernel configurations, running concurrently) give exactly what each
+    call gives alone."""
+    fdm = H.fd()
+    a = _rand_inputs([3000, 17, 800], 28, 4, 128, "f16", seed=21)      # matrix-core kernel
+    b = _rand_inputs([4096, 4096], 8, 8, 64, "bf16", layout="bhsd", seed=22)  # VALU kernel
+    ref_a = H.gpu_attention(a, 8).clone()
+    ref_b = H.gpu_attention(b, 16).clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws1 = torch.empty(fdm.fd_workspace_bytes(3, 28, 128, 8), dtype=torch.uint8, device=H.DEV)
+    ws2 = torch.empty(fdm.fd_workspace_bytes(2, 8, 64, 16), dtype=torch.uint8, device=H.DEV)
+    outs_a = [torch.empty_like(a.q) for _ in range(6)]
+    outs_b = [torch.empty_like(b.q) for _ in range(6)]
+    torch.cuda.synchronize()
+    for i in range(6):
+        fdm.fd_decode_attention(a.q, a.k, a.v, a.cu_seqlens_k, 8, out=outs_a[i], workspace=ws1,
+                                stream=s1)
+        fdm.fd_decode_attention(b.q, b.k, b.v, b.cu_seqlens_k, 16, out=outs_b[i], workspace=ws2,
+                                layout="bhsd", stream=s2)
+    torch.cuda.synchronize()
+    for i in range(6):
+        assert torch.equal(outs_a[i], ref_a), i
+        assert torch.equal(outs_b[i], ref_b), i
+
+
 def test_split_then_combine_equals_the_whole_call():
     inp = _rand_inputs([4000, 900], 32, 8, 128, "bf16")
     fd = H.fd()
