@@ -299,6 +299,33 @@ def test_concurrent_calls_on_two_streams():
         assert torch.equal(outs_b[i], ref_b), i
 
 
+@pytest.mark.parametrize("batch", [64, 65, 130])
+@pytest.mark.parametrize("dtype,dim,heads,kvh", [("bf16", 128, 16, 4), ("f16", 64, 8, 8)])
+def test_large_varlen_batches(batch, dtype, dim, heads, kvh, kernel_path):
+    """Unequal lengths (empty sequences included) at and past the batch size
+    up to which workgroups take sequences longest first (64): above it each
+    workgroup reads its sequence's offsets itself."""
+    rng = np.random.default_rng(batch + dim)
+    lengths = [int(x) for x in rng.integers(0, 600, size=batch)]
+    lengths[batch // 2] = 0
+    inp = _rand_inputs(lengths, heads, kvh, dim, dtype, seed=batch, pad=8)
+    q, k, v = H.host(inp.q), H.host(inp.k), H.host(inp.v)
+    cu = inp.cu_seqlens_k.cpu().tolist()
+    G = heads // kvh
+    for ns in (1, 3):
+        out = H.host(H.gpu_attention(inp, ns))
+        assert np.isfinite(out).all()
+        for b, L in enumerate(lengths):
+            for j in range(kvh):
+                rows = out[b, j * G:(j + 1) * G]
+                if L == 0:
+                    assert not rows.any(), (ns, b, j)
+                    continue
+                ref = oracle.attention_rows(q[b, j * G:(j + 1) * G], k[cu[b]:cu[b + 1], j],
+                                            v[cu[b]:cu[b + 1], j], 1.0 / math.sqrt(dim))
+                assert H.max_err(rows, ref) <= H.TOL[dtype], (ns, b, j, L)
+
+
 def test_split_then_combine_equals_the_whole_call():
     inp = _rand_inputs([4000, 900], 32, 8, 128, "bf16")
     fd = H.fd()
