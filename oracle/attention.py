@@ -59,7 +59,6 @@ __all__ = [
     "attention_partials",
     "attention_split_merge",
     "head_pairs",
-    "default_scale",
     "split_bounds_ceil",
     "split_states_rows",
     "merge_states",
@@ -252,11 +251,6 @@ def attention_split_merge(q, k, v, cu_seqlens_k, heads: int, kv_heads: int,
                 continue
             out[b, h:h + 1, :] = merge_partials(o_parts[b, h:h + 1], lse[b, :, h:h + 1])
     return out
-
-
-def default_scale(dim: int) -> float:
-    """1/sqrt(dim), the default of flash_decode_splitk.py."""
-    return 1.0 / math.sqrt(dim)
 
 
 # --------------------------------------------------------------------------
