@@ -110,8 +110,8 @@ def fd_last_error() -> str:
 
 
 def fd_set_kernel_path(path: int) -> int:
-    """Select the split kernel (FD_PATH_AUTO / _VALU / _MFMA / _UNPACKED);
-    returns the previous setting."""
+    """Select the split kernel (FD_PATH_AUTO / _VALU / _MFMA / _UNPACKED) for
+    later calls from this thread; returns the previous setting."""
     prev = load_library().fd_set_kernel_path(int(path))
     if prev < 0:
         raise ValueError(f"unknown kernel path {path}")
@@ -131,11 +131,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _stream(stream, device):
+def _torch_stream(stream, device):
+    """The stream the kernels run on, as a torch stream: None -> torch's
+    current stream of `device`; a raw hipStream_t handle (int) is wrapped."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _handle(ts):
+    return ctypes.c_void_p(ts.cuda_stream)
 
 
 def kv_layout(k, layout: str = "packed"):
@@ -174,12 +182,12 @@ def fd_plan_splits(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, 
     return out.value
 
 
-def fd_workspace_bytes(batch: int, heads: int, dim: int, num_splits: int) -> int:
-    return int(load_library().fd_workspace_bytes(batch, heads, dim, num_splits))
+def fd_workspace_bytes(batch: int, heads: int, num_splits: int, dim: int) -> int:
+    return int(load_library().fd_workspace_bytes(batch, heads, num_splits, dim))
 
 
-def fd_workspace_bytes_unnorm(batch: int, heads: int, dim: int, num_splits: int) -> int:
-    return int(load_library().fd_workspace_bytes_unnorm(batch, heads, dim, num_splits))
+def fd_workspace_bytes_unnorm(batch: int, heads: int, num_splits: int, dim: int) -> int:
+    return int(load_library().fd_workspace_bytes_unnorm(batch, heads, num_splits, dim))
 
 
 # Axis of the KV-head index in K/V, per layout name of kv_layout.
@@ -223,7 +231,7 @@ def _check_out(out, q):
 def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
     import torch
     size = fd_workspace_bytes_unnorm if unnorm else fd_workspace_bytes
-    need = size(batch, heads, dim, num_splits)
+    need = size(batch, heads, num_splits, dim)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
@@ -246,32 +254,41 @@ def _attention(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, out, work
                stream):
     import torch
     batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
-    if num_splits is None:
-        num_splits = _plan_from_device_lengths(q, cu_seqlens_k, heads, kv_heads, dim)
+    if out is not None:
+        _check_out(out, q)
+    lay = kv_layout(k, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
-    if out is None:
-        out = torch.empty_like(q)
-    _check_out(out, q)
-    if num_splits > 1:
-        workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
-    lay = kv_layout(k, layout)
+    ts = _torch_stream(stream, q.device)
+    # Buffers made here (out, workspace) belong to the stream the kernels
+    # run on, so the caching allocator cannot hand them to work on another
+    # stream while these kernels still use them.
+    with torch.cuda.stream(ts):
+        if num_splits is None:
+            num_splits = _plan_from_device_lengths(q, cu_seqlens_k, heads, kv_heads, dim)
+        if out is None:
+            out = torch.empty_like(q)
+        if num_splits > 1:
+            workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
     _check(getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
-        int(num_splits), float(scale), _ptr(out), _ptr(workspace), _stream(stream, q.device),
+        int(num_splits), float(scale), _ptr(out), _ptr(workspace), _handle(ts),
         _dtype_code(q), ctypes.byref(lay)), name)
     return out
 
 
 def _split(name, unnorm, q, k, v, cu_seqlens_k, num_splits, scale, workspace, layout, stream):
+    import torch
     batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
-    workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
     lay = kv_layout(k, layout)
+    ts = _torch_stream(stream, q.device)
+    with torch.cuda.stream(ts):
+        workspace = _workspace(q, batch, heads, dim, num_splits, workspace, unnorm)
     _check(getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
-        int(num_splits), float(scale), _ptr(workspace), _stream(stream, q.device),
+        int(num_splits), float(scale), _ptr(workspace), _handle(ts),
         _dtype_code(q), ctypes.byref(lay)), name)
     return workspace
 
@@ -280,13 +297,13 @@ def _combine(name, workspace, batch, heads, dim, num_splits, out, stream):
     if tuple(out.shape) != (batch, heads, dim) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [batch, heads, dim] tensor")
     size = fd_workspace_bytes_unnorm if name.endswith("_unnorm") else fd_workspace_bytes
-    if workspace.numel() * workspace.element_size() < size(batch, heads, dim, num_splits):
+    if workspace.numel() * workspace.element_size() < size(batch, heads, num_splits, dim):
         raise ValueError("workspace smaller than the split launch wrote")
     if workspace.device != out.device:
         raise ValueError("workspace and out must be on one device")
     _check(getattr(load_library(), name)(
         _ptr(workspace), batch, heads, dim, int(num_splits), _ptr(out),
-        _stream(stream, out.device), _dtype_code(out)), name)
+        _handle(_torch_stream(stream, out.device)), _dtype_code(out)), name)
     return out
 
 

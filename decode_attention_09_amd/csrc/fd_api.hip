@@ -23,7 +23,9 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
-std::atomic<int> g_path{FD_PATH_AUTO};
+// Split-kernel choice of fd_set_kernel_path: per thread, so callers on
+// different threads never steer each other's launches.
+thread_local int g_path = FD_PATH_AUTO;
 
 // The library's own choice of split kernel: matrix-core QK^T wherever that
 // kernel exists (16-bit inputs, head dim 128) and the group has at least 2
@@ -224,7 +226,7 @@ int split_impl(Format fmt, const void* q, const void* k, const void* v,
                const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
                int num_splits, float scale, void* workspace, void* stream, int dtype,
                const fd_kv_layout* layout) {
-  const int path = g_path.load(std::memory_order_relaxed);
+  const int path = g_path;
   Sizes sz;
   int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
   if (st != FD_OK) return st;
@@ -269,7 +271,7 @@ int attention_impl(Format fmt, const void* q, const void* k, const void* v,
                    const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
                    int num_splits, float scale, void* out, void* workspace, void* stream,
                    int dtype, const fd_kv_layout* layout) {
-  const int path = g_path.load(std::memory_order_relaxed);
+  const int path = g_path;
   Sizes sz;
   int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
   if (st != FD_OK) return st;
@@ -297,7 +299,7 @@ int attention_impl(Format fmt, const void* q, const void* k, const void* v,
 
 extern "C" {
 
-size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits) {
+size_t fd_workspace_bytes(int batch, int heads, int num_splits, int dim) {
   if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS || !dim_ok(dim))
     return 0;
   const double est = (double)batch * heads * num_splits * (dim + 2) * 4.0;
@@ -305,7 +307,7 @@ size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits) {
   return workspace_bytes(kNormalised, batch, heads, dim, num_splits);
 }
 
-size_t fd_workspace_bytes_unnorm(int batch, int heads, int dim, int num_splits) {
+size_t fd_workspace_bytes_unnorm(int batch, int heads, int num_splits, int dim) {
   if (batch < 1 || heads < 1 || num_splits < 1 || num_splits > FD_MAX_SPLITS || !dim_ok(dim))
     return 0;
   const double est = (double)batch * heads * num_splits * (dim + 2) * 4.0;
@@ -433,7 +435,9 @@ int fd_set_kernel_path(int path) {
   if (path != FD_PATH_AUTO && path != FD_PATH_VALU && path != FD_PATH_MFMA &&
       path != FD_PATH_UNPACKED)
     return -1;
-  return g_path.exchange(path);
+  const int prev = g_path;
+  g_path = path;
+  return prev;
 }
 
 }  // extern "C"

@@ -135,7 +135,7 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
  * part_shape / lse_shape of decode_attention_splitkv.py, in fp32. Its
  * contents before a call do not matter.
  */
-size_t fd_workspace_bytes(int batch, int heads, int dim, int num_splits);
+size_t fd_workspace_bytes(int batch, int heads, int num_splits, int dim);
 
 /*
  * fd_decode_attention -- the whole hot path: split kernel + LSE combine.
@@ -210,7 +210,7 @@ int fd_decode_combine(const void* workspace, int batch, int heads, int dim,
  * the layouts of ACC_BUF ([bh, ns, dim]) and M_BUF / L_BUF ([bh, ns]). 0 on
  * bad sizes.
  */
-size_t fd_workspace_bytes_unnorm(int batch, int heads, int dim, int num_splits);
+size_t fd_workspace_bytes_unnorm(int batch, int heads, int num_splits, int dim);
 
 /* fd_decode_split_unnorm -- split launch only, writing (ACC, M, L) into
  * `workspace` (fd_workspace_bytes_unnorm bytes, required). */
@@ -235,9 +235,10 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
                                const fd_kv_layout* layout);
 
 /*
- * fd_set_kernel_path -- which split kernel later calls launch, process-wide
- * (for benchmarks and tests that compare the two; calls already enqueued are
- * unaffected). FD_PATH_VALU: vector-ALU dot products (v_dot2 / FMA) for
+ * fd_set_kernel_path -- which split kernel later calls made from the calling
+ * thread launch (a per-thread setting, for benchmarks and tests that compare
+ * the kernels; other threads and calls already enqueued are unaffected; a
+ * new thread starts at FD_PATH_AUTO). FD_PATH_VALU: vector-ALU dot products (v_dot2 / FMA) for
  * QK^T and PV everywhere. FD_PATH_MFMA: QK^T on the matrix cores
  * (v_mfma_f32_16x16x32_{f16,bf16}) wherever that kernel exists -- fp16/bf16
  * at head dim 128 -- and the VALU kernel elsewhere. FD_PATH_AUTO (the

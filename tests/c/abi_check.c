@@ -18,9 +18,14 @@ int main(void) {
   st = fd_plan_splits(2, 8, 1, 128, FD_F16, empty, 256, 0, &ns);
   printf("plan_empty %d\n", st);
 
-  printf("ws %zu\n", fd_workspace_bytes(2, 8, 128, 4));
-  printf("ws_unnorm %zu\n", fd_workspace_bytes_unnorm(2, 8, 128, 4));
-  printf("ws_bad %zu\n", fd_workspace_bytes(1, 8, 100, 4));
+  printf("ws %zu\n", fd_workspace_bytes(2, 8, 4, 128));
+  /* argument order (batch, heads, num_splits, dim): 128 splits of dim 64
+   * and 64 splits of dim 128 need different sizes, so a swap shows */
+  printf("ws_order %zu %zu\n", fd_workspace_bytes(1, 1, 128, 64), fd_workspace_bytes(1, 1, 64, 128));
+  printf("ws_unnorm %zu\n", fd_workspace_bytes_unnorm(2, 8, 4, 128));
+  printf("ws_unnorm_order %zu %zu\n", fd_workspace_bytes_unnorm(1, 1, 128, 64),
+         fd_workspace_bytes_unnorm(1, 1, 64, 128));
+  printf("ws_bad %zu\n", fd_workspace_bytes(1, 8, 4, 100));
 
   /* argument checks run before anything touches the device */
   st = fd_decode_attention(NULL, NULL, NULL, NULL, 1, 8, 1, 128, 2, 0.1f, NULL, NULL, NULL,

@@ -84,9 +84,9 @@ int main(void) {
     CHECK(ns <= min_len, "ns %d > shortest sequence %d", ns, (int)min_len);
 
     /* workspace sizes: zero for bad arguments, monotone in the split count */
-    const size_t w1 = fd_workspace_bytes(batch, heads, dim, ns);
-    const size_t w2 = fd_workspace_bytes(batch, heads, dim, ns + 1 <= FD_MAX_SPLITS ? ns + 1 : ns);
-    const size_t u1 = fd_workspace_bytes_unnorm(batch, heads, dim, ns);
+    const size_t w1 = fd_workspace_bytes(batch, heads, ns, dim);
+    const size_t w2 = fd_workspace_bytes(batch, heads, ns + 1 <= FD_MAX_SPLITS ? ns + 1 : ns, dim);
+    const size_t u1 = fd_workspace_bytes_unnorm(batch, heads, ns, dim);
     calls += 3;
     CHECK(w1 > 0 && w2 >= w1 && u1 >= w1, "workspace %zu %zu %zu", w1, w2, u1);
     CHECK(w1 >= (size_t)batch * heads * ns * ((size_t)dim + 1) * 4, "workspace too small");
@@ -101,9 +101,9 @@ int main(void) {
   CHECK(fd_plan_splits(1, 8, 1, 128, 7, lens, 256, 0, &ns) == FD_ERR_UNSUPPORTED, "dtype 7");
   CHECK(fd_plan_splits(1, 8, 1, 128, FD_F16, NULL, 256, 0, &ns) == FD_ERR_INVALID_ARG, "null");
   CHECK(fd_plan_splits(1, 8, 1, 128, FD_F16, lens, -1, 0, &ns) == FD_ERR_INVALID_ARG, "cus -1");
-  CHECK(fd_workspace_bytes(INT32_MAX, INT32_MAX, 128, FD_MAX_SPLITS) == 0, "overflow size");
-  CHECK(fd_workspace_bytes(1, 1, 128, FD_MAX_SPLITS + 1) == 0, "too many splits");
-  CHECK(fd_workspace_bytes_unnorm(1, 1, 100, 2) == 0, "bad dim");
+  CHECK(fd_workspace_bytes(INT32_MAX, INT32_MAX, FD_MAX_SPLITS, 128) == 0, "overflow size");
+  CHECK(fd_workspace_bytes(1, 1, FD_MAX_SPLITS + 1, 128) == 0, "too many splits");
+  CHECK(fd_workspace_bytes_unnorm(1, 1, 2, 100) == 0, "bad dim");
   calls += 9;
   for (int s = -2; s < 8; ++s) CHECK(fd_status_string(s) != NULL, "status string %d", s);
 

@@ -70,24 +70,39 @@ def oracle_full(inp: W.Inputs, ns: int | None = None, scale=None):
     return oracle.attention_direct(q, k, v, cu, w.heads, w.kv_heads, sc, layout=w.layout)
 
 
-def oracle_pairs(inp: W.Inputs, pairs, scale=None):
-    """Oracle rows for a few (b, kv_head) pairs, copying only their K/V rows
-    to the host. Returns {(b, kvh): o [G, D]}."""
+def oracle_pairs(inp: W.Inputs, pairs, scale=None, workers: int = 1):
+    """Oracle rows for (b, kv_head) pairs, copying only their K/V rows to the
+    host, one pair at a time. With workers > 1 the oracle evaluations run in
+    a thread pool (numpy releases the GIL) while the next pair is copied.
+    Returns {(b, kvh): o [G, D]}."""
+    from concurrent.futures import ThreadPoolExecutor
     w = inp.workload
     G = w.group
     sc = w.sm_scale if scale is None else scale
     cu = inp.cu_seqlens_k.cpu().tolist()
-    res = {}
-    for b, j in pairs:
+
+    def rows(b, j):
         L = cu[b + 1] - cu[b]
         if w.layout == "packed":
-            kr = host(inp.k[cu[b]:cu[b + 1], j, :])
-            vr = host(inp.v[cu[b]:cu[b + 1], j, :])
-        else:
-            kr = host(inp.k[b, j, :L, :])
-            vr = host(inp.v[b, j, :L, :])
-        qr = host(inp.q[b, j * G:(j + 1) * G, :])
-        res[(b, j)] = oracle.attention_rows(qr, kr, vr, sc)
+            return host(inp.k[cu[b]:cu[b + 1], j, :]), host(inp.v[cu[b]:cu[b + 1], j, :])
+        return host(inp.k[b, j, :L, :]), host(inp.v[b, j, :L, :])
+
+    res = {}
+    with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        futs, pending = {}, []
+        for n, (b, j) in enumerate(pairs):
+            kr, vr = rows(b, j)
+            qr = host(inp.q[b, j * G:(j + 1) * G, :])
+            f = ex.submit(oracle.attention_rows, qr, kr, vr, sc)
+            futs[(b, j)] = f
+            pending.append(f)
+            del kr, vr
+            if len(pending) >= 2 * max(1, workers):   # bound the host copies held
+                pending.pop(0).result()
+            if (n + 1) % 16 == 0:
+                announce(f"  oracle pairs copied: {n + 1}/{len(pairs)}")
+        for key, f in futs.items():
+            res[key] = f.result()
     return res
 
 

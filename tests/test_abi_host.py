@@ -58,7 +58,7 @@ def test_status_strings():
 @pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (32, 28, 128, 8),
                                       (3, 5, 64, 1000)])
 def test_workspace_bytes_layout(B, H, D, ns):
-    n = fd.fd_workspace_bytes(B, H, D, ns)
+    n = fd.fd_workspace_bytes(B, H, ns, D)
     opart = B * H * ns * D * 4
     lse_off = (opart + 255) // 256 * 256
     assert n == lse_off + B * ns * H * 4
@@ -67,20 +67,20 @@ def test_workspace_bytes_layout(B, H, D, ns):
 @pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (3, 5, 64, 1000)])
 def test_workspace_bytes_unnorm_layout(B, H, D, ns):
     # ACC [B,H,ns,D], then M [B,H,ns] and L [B,H,ns], each at a 256-B boundary
-    n = fd.fd_workspace_bytes_unnorm(B, H, D, ns)
+    n = fd.fd_workspace_bytes_unnorm(B, H, ns, D)
     rows = B * H * ns
     off_m = (rows * D * 4 + 255) // 256 * 256
     off_l = off_m + (rows * 4 + 255) // 256 * 256
     assert n == off_l + rows * 4
-    assert fd.fd_workspace_bytes_unnorm(0, H, D, ns) == 0
-    assert fd.fd_workspace_bytes_unnorm(B, H, 96, ns) == 0
+    assert fd.fd_workspace_bytes_unnorm(0, H, ns, D) == 0
+    assert fd.fd_workspace_bytes_unnorm(B, H, ns, 96) == 0
 
 
 def test_workspace_bytes_rejects_bad_sizes():
-    assert fd.fd_workspace_bytes(0, 8, 128, 4) == 0
-    assert fd.fd_workspace_bytes(1, 8, 100, 4) == 0
-    assert fd.fd_workspace_bytes(1, 8, 128, 0) == 0
-    assert fd.fd_workspace_bytes(1, 8, 128, fd.FD_MAX_SPLITS + 1) == 0
+    assert fd.fd_workspace_bytes(0, 8, 4, 128) == 0
+    assert fd.fd_workspace_bytes(1, 8, 4, 100) == 0
+    assert fd.fd_workspace_bytes(1, 8, 0, 128) == 0
+    assert fd.fd_workspace_bytes(1, 8, fd.FD_MAX_SPLITS + 1, 128) == 0
 
 
 # ----------------------------------------------------------------- planner --
@@ -233,6 +233,32 @@ def test_kernel_path_setting():
         fd.fd_set_kernel_path(9)
 
 
+def test_kernel_path_setting_is_per_thread():
+    """Each thread steers only its own calls: a setting made on one thread is
+    not seen by another, and a new thread starts at FD_PATH_AUTO."""
+    import threading
+    seen = {}
+    gate = threading.Barrier(2)
+
+    def worker(name, path):
+        first = fd.fd_set_kernel_path(path)
+        gate.wait()                       # both threads have set their path
+        seen[name] = (first, fd.fd_set_kernel_path(first))
+
+    main_prev = fd.fd_set_kernel_path(fd.FD_PATH_UNPACKED)
+    try:
+        ts = [threading.Thread(target=worker, args=("a", fd.FD_PATH_VALU)),
+              threading.Thread(target=worker, args=("b", fd.FD_PATH_MFMA))]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    finally:
+        assert fd.fd_set_kernel_path(main_prev) == fd.FD_PATH_UNPACKED
+    assert seen == {"a": (fd.FD_PATH_AUTO, fd.FD_PATH_VALU),
+                    "b": (fd.FD_PATH_AUTO, fd.FD_PATH_MFMA)}
+
+
 # ------------------------------------------- binding argument marshalling --
 def _cpu_inputs(B=2, H=8, Hkv=2, D=64, T=40):
     import torch
@@ -275,7 +301,7 @@ def test_binding_refuses_mismatched_tensors_before_any_call():
 def test_binding_refuses_a_short_workspace_or_wrong_out_in_combine():
     import torch
     out = torch.zeros(2, 8, 64, dtype=torch.float16)
-    need = fd.fd_workspace_bytes(2, 8, 64, 3)
+    need = fd.fd_workspace_bytes(2, 8, 3, 64)
     with pytest.raises(ValueError):
         fd.fd_decode_combine(torch.zeros(need - 1, dtype=torch.uint8), 2, 8, 64, 3, out)
     with pytest.raises(ValueError):

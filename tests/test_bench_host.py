@@ -67,3 +67,15 @@ def test_split_workgroups_counts_row_chunks_and_splits():
     assert bench.split_workgroups(llama, 2, 1) == 16 * 8 * 4 * 2   # unpacked: one row each
     varlen = W.varlen_qwen()              # 4 KV heads, group 7
     assert bench.split_workgroups(varlen, 8, 8) == 32 * 4 * 8
+
+
+def test_default_workload_is_the_largest_configuration():
+    """The bench line runs the largest single-GPU workload: Llama-3.1-8B
+    shape at batch 16 and 131,072 keys (8.59 GB of K/V per call)."""
+    def kv_bytes(w):
+        assert w.kv_len is not None or w.varlen_range is not None
+        keys = w.batch * (w.kv_len if w.kv_len is not None else w.varlen_range[1])
+        return keys * w.kv_heads * w.dim * 2 * w.elem_bytes
+    biggest = max(W.all_workloads(), key=kv_bytes)
+    assert bench.DEFAULT_WORKLOAD == biggest.name == "llama8b_b16_l131072_h32kv8_d128_bf16"
+    assert kv_bytes(biggest) == 16 * 131072 * 8 * 128 * 2 * 2

@@ -43,6 +43,11 @@ def test_c_program(c_program):
     assert int(out["ws_unnorm"]) == ((rows * 128 * 4 + 255) // 256 * 256
                                      + (rows * 4 + 255) // 256 * 256 + rows * 4)
     assert out["ws_bad"] == "0"
+    # (batch, heads, num_splits, dim): 128 splits at dim 64, then 64 splits at dim 128
+    a, b = (int(x) for x in out["ws_order"].split())
+    assert a == 128 * 64 * 4 + 128 * 4 and b == 64 * 128 * 4 + 64 * 4 and a != b
+    a, b = (int(x) for x in out["ws_unnorm_order"].split())
+    assert a == 128 * 64 * 4 + 2 * 128 * 4 and b == 64 * 128 * 4 + 256 + 64 * 4
     assert out["null_args"] == "1"
     assert out["bad_dim"] == "2"
     assert out["nan_scale"] == "1"

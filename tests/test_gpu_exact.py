@@ -283,8 +283,8 @@ def test_concurrent_calls_on_two_streams():
     ref_a = H.gpu_attention(a, 8).clone()
     ref_b = H.gpu_attention(b, 16).clone()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    ws1 = torch.empty(fdm.fd_workspace_bytes(3, 28, 128, 8), dtype=torch.uint8, device=H.DEV)
-    ws2 = torch.empty(fdm.fd_workspace_bytes(2, 8, 64, 16), dtype=torch.uint8, device=H.DEV)
+    ws1 = torch.empty(fdm.fd_workspace_bytes(3, 28, 8, 128), dtype=torch.uint8, device=H.DEV)
+    ws2 = torch.empty(fdm.fd_workspace_bytes(2, 8, 16, 64), dtype=torch.uint8, device=H.DEV)
     outs_a = [torch.empty_like(a.q) for _ in range(6)]
     outs_b = [torch.empty_like(b.q) for _ in range(6)]
     torch.cuda.synchronize()
@@ -297,6 +297,75 @@ def test_concurrent_calls_on_two_streams():
     for i in range(6):
         assert torch.equal(outs_a[i], ref_a), i
         assert torch.equal(outs_b[i], ref_b), i
+
+
+def test_default_buffers_belong_to_the_call_stream():
+    """With stream=s given outside any stream context and no workspace or
+    out, the binding's own buffers are allocated on s. Memory that torch
+    then hands out on the default stream while s still runs cannot be the
+    workspace: scribbling over such blocks leaves the result exact."""
+    fdm = H.fd()
+    inp = _rand_inputs([16384] * 8, 32, 8, 128, "bf16", seed=31)
+    ns = 16
+    ref = H.gpu_attention(inp, ns).clone()
+    need = fdm.fd_workspace_bytes(8, 32, ns, 128)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(fdm.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns, stream=s))
+        # the call's temporaries are freed on return; grab blocks of the same
+        # size on the default stream and overwrite them at once
+        junk = [torch.empty(need, dtype=torch.uint8, device=H.DEV) for _ in range(4)]
+        for j in junk:
+            j.fill_(0xFF)
+        del junk
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
+def test_kernel_path_per_thread_calls():
+    """Two threads, each with its own kernel path and stream, calling at the
+    same time: each gets its own path's result, bitwise (the VALU and the
+    matrix-core kernels round differently, so a crossed setting shows)."""
+    import threading
+    fdm = H.fd()
+    inp = _rand_inputs([5000, 3000, 4100], 32, 4, 128, "bf16", seed=33)
+    refs = {}
+    for name, path in (("valu", fdm.FD_PATH_VALU), ("mfma", fdm.FD_PATH_MFMA)):
+        prev = fdm.fd_set_kernel_path(path)
+        refs[name] = H.gpu_attention(inp, 8).clone()
+        fdm.fd_set_kernel_path(prev)
+    assert not torch.equal(refs["valu"], refs["mfma"])
+    got, errors = {}, []
+    gate = threading.Barrier(2)
+
+    def worker(name, path):
+        try:
+            fdm.fd_set_kernel_path(path)
+            s = torch.cuda.Stream()
+            outs = []
+            gate.wait()
+            for _ in range(20):
+                outs.append(fdm.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 8,
+                                                    stream=s))
+            s.synchronize()
+            got[name] = outs
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=("valu", fdm.FD_PATH_VALU)),
+          threading.Thread(target=worker, args=("mfma", fdm.FD_PATH_MFMA))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    for name in ("valu", "mfma"):
+        assert len(got[name]) == 20
+        for o in got[name]:
+            assert torch.equal(o, refs[name]), name
 
 
 @pytest.mark.parametrize("batch", [64, 65, 130])
@@ -379,7 +448,7 @@ def test_whole_call_matches_split_then_combine_over_many_calls(lens, heads, kvh,
     ws2 = fd.fd_decode_split(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns)
     ref = torch.empty_like(inp.q)
     fd.fd_decode_combine(ws2, len(lens), heads, dim, ns, ref)
-    ws = torch.empty(fd.fd_workspace_bytes(len(lens), heads, dim, ns), dtype=torch.uint8,
+    ws = torch.empty(fd.fd_workspace_bytes(len(lens), heads, ns, dim), dtype=torch.uint8,
                      device=H.DEV)
     outs = [fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns, workspace=ws)
             for _ in range(50)]

@@ -38,7 +38,7 @@ def test_graph_replays_match_eager(case):
     q_buf = inp.q.clone()
     call = fdm.fd_decode_attention_unnorm if unnorm else fdm.fd_decode_attention
     wsize = (fdm.fd_workspace_bytes_unnorm if unnorm else fdm.fd_workspace_bytes)(
-        len(lengths), heads, dim, ns)
+        len(lengths), heads, ns, dim)
     ws = torch.empty(max(1, wsize), dtype=torch.uint8, device=H.DEV)
     out_g = torch.empty_like(inp.q)
 

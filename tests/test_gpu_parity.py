@@ -86,9 +86,11 @@ def test_unpacked_comparator_shapes(batch, kv_len):
 @pytest.mark.parametrize("kv_len", W.LLAMA_LENS)
 @pytest.mark.parametrize("batch", W.LLAMA_BATCHES)
 def test_llama_long_context(batch, kv_len):
-    """32/8 heads, d=128, bf16, split count from the planner; the batch-16
-    runs at 32K and 128K keys (2-8.6 GB of KV) compare sampled
-    (sequence, KV head) pairs with the oracle, the others the whole batch."""
+    """32/8 heads, d=128, bf16, split count from the planner, in the launch
+    configuration the benchmark times. Up to 16 x 8K keys the whole batch is
+    compared at once; above that (2.1 and 8.6 GB of KV at batch 16) every
+    (sequence, KV head) pair is compared, its K/V rows copied to the host one
+    pair at a time."""
     w = W.llama(batch, kv_len)
     inp = W.make_inputs(w, H.DEV)
     fd = H.fd()
@@ -98,13 +100,14 @@ def test_llama_long_context(batch, kv_len):
     else:
         out = H.host(H.gpu_attention(inp, ns))
         assert np.isfinite(out).all()
-        rng = np.random.default_rng(1)
-        pairs = sorted({(int(rng.integers(batch)), int(rng.integers(8))) for _ in range(5)})
-        pairs += [(0, 0), (batch - 1, 7)]
-        refs = H.oracle_pairs(inp, pairs)
+        pairs = [(b, j) for b in range(batch) for j in range(w.kv_heads)]
+        refs = H.oracle_pairs(inp, pairs, workers=8)
+        worst = 0.0
         for (b, j), ref in refs.items():
             err = H.max_err(out[b, j * 4:(j + 1) * 4], ref)
+            worst = max(worst, err)
             assert err <= H.TOL["bf16"], (b, j, err)
+        print(f"  {w.name} ns={ns}: {len(pairs)} pairs, max_abs_err={worst:.3e}", flush=True)
     del inp
     torch.cuda.empty_cache()
 
