@@ -18,14 +18,16 @@ __all__ = [
     "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path", "kv_layout",
     "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "FD_PATH_UNPACKED", "workspace_views",
     "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
-    "fd_decode_attention_unnorm", "workspace_views_unnorm",
+    "fd_decode_attention_unnorm", "workspace_views_unnorm", "fd_decode_attention_noalloc",
+    "FD_NOALLOC_SCRATCH_BYTES",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_MAX_SPLITS = 16384
+FD_NOALLOC_SCRATCH_BYTES = 16 << 20
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA, FD_PATH_UNPACKED = 0, 1, 2, 3
 _STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
-           3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP"}
+           3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP", 5: "FD_ERR_SCRATCH"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -36,7 +38,7 @@ class FdError(RuntimeError):
         self.status = status
         lib = load_library()
         msg = lib.fd_status_string(status).decode()
-        extra = lib.fd_last_error().decode() if status == 4 else ""
+        extra = lib.fd_last_error().decode() if status in (4, 5) else ""
         super().__init__(f"{where}: {_STATUS.get(status, status)} ({msg}) {extra}".strip())
 
 
@@ -86,6 +88,9 @@ def load_library():
     lib.fd_decode_split_unnorm.restype = i32
     lib.fd_decode_combine_unnorm.argtypes = lib.fd_decode_combine.argtypes
     lib.fd_decode_combine_unnorm.restype = i32
+    lib.fd_decode_attention_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp,
+                                                vp, i32, lay]
+    lib.fd_decode_attention_noalloc.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -329,6 +334,25 @@ def fd_decode_combine(workspace, batch: int, heads: int, dim: int, num_splits: i
                       stream=None):
     """Second launch only: merge the workspace into out [batch, heads, dim]."""
     return _combine("fd_decode_combine", workspace, batch, heads, dim, num_splits, out, stream)
+
+
+def fd_decode_attention_noalloc(q, k, v, cu_seqlens_k, num_splits: int, out,
+                                scale: float | None = None, layout: str = "packed", stream=None):
+    """fd_decode_attention without a workspace: the partials go to the
+    library's static per-GPU scratch (FD_NOALLOC_SCRATCH_BYTES). Nothing is
+    allocated, here or in the library: `out` and `num_splits` are required.
+    Calls that overlap in time on one GPU share that scratch and race."""
+    batch, heads, kv_heads, dim = _sizes(q, k, v, cu_seqlens_k, layout)
+    _check_out(out, q)
+    lay = kv_layout(k, layout)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    name = "fd_decode_attention_noalloc"
+    _check(getattr(load_library(), name)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_k), batch, heads, kv_heads, dim,
+        int(num_splits), float(scale), _ptr(out), _handle(_torch_stream(stream, q.device)),
+        _dtype_code(q), ctypes.byref(lay)), name)
+    return out
 
 
 def fd_decode_attention_unnorm(q, k, v, cu_seqlens_k, num_splits: int | None,

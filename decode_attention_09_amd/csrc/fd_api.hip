@@ -16,9 +16,17 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fd.h"
 #include "fd_internal.h"
+
+// Partials of fd_decode_attention_noalloc: one array per GPU, resident from
+// module load until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on the current GPU comes
+// from hipGetSymbolAddress (scratch_on_device below) and only that address
+// is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[FD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -73,6 +81,39 @@ int device_cus(int* cus) {
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
   *cus = c;
+  return FD_OK;
+}
+
+// Device address of `scratch` on the current GPU, looked up once per device
+// (with that device current) and cached.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "device ordinal %d beyond %d", dev,
+                  kMaxDevices);
+    return FD_ERR_UNSUPPORTED;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "scratch address %p not 256-B aligned",
+                      p);
+        return FD_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
   return FD_OK;
 }
 
@@ -267,22 +308,31 @@ int combine_impl(Format fmt, const void* workspace, int batch, int heads, int di
   return FD_OK;
 }
 
+// Checks of a whole-call entry point other than its workspace.
+int check_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,
+                    int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
+                    const void* out, int dtype, const fd_kv_layout* layout, int path, Sizes* sz,
+                    fd_kv_layout* L) {
+  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, sz, rows_per_pass(path));
+  if (st != FD_OK) return st;
+  if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
+  return check_layout(layout, kv_heads, dim, dtype, L);
+}
+
 int attention_impl(Format fmt, const void* q, const void* k, const void* v,
                    const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
                    int num_splits, float scale, void* out, void* workspace, void* stream,
                    int dtype, const fd_kv_layout* layout) {
   const int path = g_path;
   Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
-  if (st != FD_OK) return st;
-  if (!q || !k || !v || !cu_seqlens_k || !out) return FD_ERR_INVALID_ARG;
-  if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FD_ERR_INVALID_ARG;
-  if (workspace && !aligned16(workspace)) return FD_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return FD_ERR_INVALID_ARG;
   fd_kv_layout L;
-  st = check_layout(layout, kv_heads, dim, dtype, &L);
+  int st = check_attention(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
+                           out, dtype, layout, path, &sz, &L);
   if (st != FD_OK) return st;
+  if (num_splits > 1 && !workspace) return FD_ERR_INVALID_ARG;
+  if (workspace && !aligned16(workspace)) return FD_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (num_splits == 1) {
     // one split is the whole sequence under either bound rule: one launch
@@ -418,6 +468,31 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
                         scale, out, workspace, stream, dtype, layout);
 }
 
+int fd_decode_attention_noalloc(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads,
+                                int dim, int num_splits, float scale, void* out, void* stream,
+                                int dtype, const fd_kv_layout* layout) {
+  Sizes sz;
+  fd_kv_layout L;
+  const int st = check_attention(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
+                                 scale, out, dtype, layout, g_path, &sz, &L);
+  if (st != FD_OK) return st;
+  void* ws = nullptr;
+  if (num_splits > 1) {
+    const size_t need = workspace_bytes(kNormalised, batch, heads, dim, num_splits);
+    if (need > FD_NOALLOC_SCRATCH_BYTES) {
+      std::snprintf(g_last_error, sizeof(g_last_error),
+                    "the partials need %zu bytes, the static scratch holds %zu", need,
+                    (size_t)FD_NOALLOC_SCRATCH_BYTES);
+      return FD_ERR_SCRATCH;
+    }
+    const int s2 = scratch_on_device(&ws);
+    if (s2 != FD_OK) return s2;
+  }
+  return attention_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim,
+                        num_splits, scale, out, ws, stream, dtype, layout);
+}
+
 const char* fd_status_string(int status) {
   switch (status) {
     case FD_OK: return "ok";
@@ -425,6 +500,7 @@ const char* fd_status_string(int status) {
     case FD_ERR_UNSUPPORTED: return "unsupported configuration";
     case FD_ERR_EMPTY_SPLIT: return "a sequence has no key (empty split)";
     case FD_ERR_HIP: return "HIP runtime error";
+    case FD_ERR_SCRATCH: return "the call needs more than the static scratch holds";
     default: return "unknown status";
   }
 }

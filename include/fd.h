@@ -68,7 +68,9 @@ enum {
   FD_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride or alignment */
   FD_ERR_UNSUPPORTED = 2,  /* dim not in {16,32,64,128}, dtype, group > 64 */
   FD_ERR_EMPTY_SPLIT = 3,  /* planner: some sequence has no key */
-  FD_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+  FD_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
+  FD_ERR_SCRATCH = 5       /* fd_decode_attention_noalloc: the call's partials
+                              need more than FD_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Limits. */
@@ -253,11 +255,41 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
 enum { FD_PATH_AUTO = 0, FD_PATH_VALU = 1, FD_PATH_MFMA = 2, FD_PATH_UNPACKED = 3 };
 int fd_set_kernel_path(int path);
 
+/*
+ * fd_decode_attention_noalloc -- fd_decode_attention for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same kernels, arguments and result as
+ * fd_decode_attention, except that there is no workspace argument: the
+ * partials (fd_workspace_bytes(batch, heads, num_splits, dim) bytes) go to a
+ * static device array of FD_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); the caller
+ * still owns q, k, v, cu_seqlens_k and out.
+ *
+ *   - A call whose partials need more than FD_NOALLOC_SCRATCH_BYTES returns
+ *     FD_ERR_SCRATCH before launching anything (fd_last_error() says how
+ *     much it needed); num_splits == 1 needs none.
+ *   - Every call on one GPU uses that GPU's one array, whatever the stream:
+ *     calls that overlap in time on one GPU (concurrent streams, graph
+ *     replays running side by side) race on it and must be serialised by
+ *     the caller. The array keeps the last call's partials; nothing in it
+ *     needs to start at zero (each call writes every partial it reads).
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress) and caches it: make that call outside a graph
+ *     capture.
+ */
+#define FD_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fd_decode_attention_noalloc(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_k, int batch, int heads,
+                                int kv_heads, int dim, int num_splits, float scale,
+                                void* out, void* stream, int dtype,
+                                const fd_kv_layout* layout);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fd_status_string(int status);
 
-/* Last HIP error text recorded by this thread when FD_ERR_HIP was returned
- * (static per-thread buffer, "" if none). */
+/* Last error text recorded by this thread when FD_ERR_HIP or FD_ERR_SCRATCH
+ * was returned (static per-thread buffer, "" if none). */
 const char* fd_last_error(void);
 
 #ifdef __cplusplus

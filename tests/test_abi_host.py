@@ -214,6 +214,27 @@ def test_unnorm_attention_rejects_before_launch(kw, status):
     assert lib.fd_decode_combine_unnorm(16, 1, 8, 64 + 32, 2, 16, None, 1) == 2
 
 
+def test_noalloc_rejects_before_launch():
+    """fd_decode_attention_noalloc checks its arguments, then that the
+    partials fit the static scratch, before touching any device."""
+    lib = _lib()
+    args = [16, 16, 16, 16]
+    # 1 x 64 heads x 1100 splits x (128 + 1) floats > 16 MiB
+    assert fd.fd_workspace_bytes(1, 64, 1100, 128) > fd.FD_NOALLOC_SCRATCH_BYTES
+    assert lib.fd_decode_attention_noalloc(*args, 1, 64, 64, 128, 1100, 0.1, 16, None,
+                                           fd.FD_F16, None) == 5
+    assert "static scratch" in fd.fd_last_error()
+    assert lib.fd_decode_attention_noalloc(*args, 1, 64, 64, 96, 2, 0.1, 16, None,
+                                           fd.FD_F16, None) == 2
+    assert lib.fd_decode_attention_noalloc(*args, 1, 64, 63, 128, 2, 0.1, 16, None,
+                                           fd.FD_F16, None) == 1
+    assert lib.fd_decode_attention_noalloc(None, 16, 16, 16, 1, 8, 1, 128, 1, 0.1, 16, None,
+                                           fd.FD_F16, None) == 1
+    assert lib.fd_decode_attention_noalloc(*args, 1, 8, 1, 128, 2, float("nan"), 16, None,
+                                           fd.FD_F16, None) == 1
+    assert "scratch" in fd.fd_status_string(5)
+
+
 def test_split_and_combine_reject_before_launch():
     lib = _lib()
     assert lib.fd_decode_split(16, 16, 16, 16, 1, 8, 1, 128, 2, 0.1, None, None, 1, None) == 1
