@@ -27,6 +27,9 @@ SOURCES = ["fd_split_f32.hip", "fd_split_f16.hip", "fd_split_bf16.hip", "fd_comb
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the split kernels' first two arguments (cu_seqlens_k, batch) arrive
+         # preloaded in SGPRs
+         "-mllvm", "-amdgpu-kernarg-preload-count=2",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -51,6 +51,9 @@ namespace fd {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
@@ -91,6 +94,27 @@ __device__ __forceinline__ float halves_pair(float x, Op op) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return op(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// Reduce-scatter steps over the four 16-lane rows, for two values at once.
+// rows_scatter(a, b): rows 0 and 2 get a summed over their row pair (0+1,
+// 2+3), rows 1 and 3 get b summed over theirs. halves_scatter(a, b): the
+// lower half (rows 0, 1) gets a summed over the halves (row r + row r+2),
+// the upper half gets b. Applied to values x_{4j..4j+3} (rows_scatter on
+// pairs, then halves_scatter on the results), row R ends with
+// (x_{4j+R} of row 0 + of row 1) + (of row 2 + of row 3): the same sums,
+// in the same order, as rows_pair then halves_pair on each value, with a
+// quarter of the swaps and adds.
+__device__ __forceinline__ float rows_scatter(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float halves_scatter(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 // Sum over aligned groups of LPR lanes; every lane of a group gets the same
@@ -210,6 +234,20 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
     static_cast<__bf16*>(out)[idx] = (__bf16)x;
 }
 
+// Four consecutive output elements (the index is a multiple of 4).
+template <int DT>
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, const float (&x)[4]) {
+  if constexpr (DT == DT_F32) {
+    *reinterpret_cast<f4_t*>(static_cast<float*>(out) + idx) = f4_t{x[0], x[1], x[2], x[3]};
+  } else if constexpr (DT == DT_F16) {
+    *reinterpret_cast<h4_t*>(static_cast<_Float16*>(out) + idx) =
+        h4_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+  } else {
+    *reinterpret_cast<b4_t*>(static_cast<__bf16*>(out) + idx) =
+        b4_t{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  }
+}
+
 // ------------------------------------------------------- work decoding --
 // One workgroup per segment ("item"): workgroup -> (split, KV head, row
 // chunk, sequence rank), split index fastest, without memory access; then
@@ -248,7 +286,18 @@ struct LaneSeqs {
   int lo, hi, rank;
 };
 
-__device__ __forceinline__ LaneSeqs lane_seqs(const SplitArgs& a) {
+// cu_seqlens_k and the batch size. The split kernels take them as their
+// first two arguments, ahead of SplitArgs, so that they are preloaded into
+// SGPRs at wave launch (the library is built with
+// -amdgpu-kernarg-preload-count=2): the cu_seqlens_k load then starts at
+// once and overlaps the fetch of the other arguments, instead of waiting
+// for it (two dependent memory round trips before the first K/V load).
+struct SeqTable {
+  const int32_t* cu;
+  int batch;
+};
+
+__device__ __forceinline__ LaneSeqs lane_seqs(const SeqTable& a) {
   LaneSeqs s{0, 0, -1};
   if (a.batch > kLptMaxBatch) return s;
   const int lane = threadIdx.x & (kWave - 1);
@@ -283,23 +332,23 @@ struct Segment {
 // The sequence, its varlen bounds and the proportional segment
 // [L*s/ns, L*(s+1)/ns) (64-bit products) of an item.
 template <int EB>
-__device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const WorkItem& w,
-                                                  const LaneSeqs& ls) {
+__device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const SeqTable& st,
+                                                  const WorkItem& w, const LaneSeqs& ls) {
   Segment g;
   g.sid = w.sid;
   g.kvh = w.kvh;
   g.h0 = w.h0;
   g.nrows = w.nrows;
   int cu0, cu1;
-  if (a.batch <= kLptMaxBatch) {
+  if (st.batch <= kLptMaxBatch) {
     const uint64_t hit = __builtin_amdgcn_ballot_w64(ls.rank == w.rank);
     g.b = hit ? (int)__builtin_ctzll(hit) : w.rank;
     cu0 = __builtin_amdgcn_readlane(ls.lo, g.b);
     cu1 = __builtin_amdgcn_readlane(ls.hi, g.b);
   } else {
     g.b = w.rank;
-    cu0 = a.cu[g.b];
-    cu1 = a.cu[g.b + 1];
+    cu0 = st.cu[g.b];
+    cu1 = st.cu[g.b + 1];
   }
   const int ns = a.num_splits;
   const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
@@ -339,39 +388,50 @@ __device__ __forceinline__ void tile_rsrc(const Segment& sg, int j, __amdgpu_buf
 // write the split epilogue: o_s = acc / l and lse2_s = log2(l) + m, or the
 // unnormalised state (m_s, l_s, acc_s) of the MiniInfer format (m_s the
 // split's largest base-2 score), or the final output in dtype when the call
-// has a single split.
+// has a single split. Each thread takes four consecutive dims of one row
+// (one 16-byte LDS read per wave state, one vector store), so a group of 8
+// rows at D = 128 is written by 256 threads in one pass.
 template <int DT, int D, int GC, int NW>
 __device__ __forceinline__ void store_segment(const SplitArgs& a, const Segment& sg,
                                               const float (&sm_m)[NW][GC],
                                               const float (&sm_l)[NW][GC],
                                               const float (&sm_acc)[NW][GC][D]) {
+  constexpr int Q = D / 4;  // groups of four dims per row
   const int ns = a.num_splits;
-  for (int idx = threadIdx.x; idx < sg.nrows * D; idx += NW * kWave) {
-    const int g = idx / D;
-    const int d = idx % D;
+  for (int idx = threadIdx.x; idx < sg.nrows * Q; idx += NW * kWave) {
+    const int g = idx / Q;
+    const int d = (idx % Q) * 4;
     float M = sm_m[0][g];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
-    float lsum = 0.0f, o = 0.0f;
+    float lsum = 0.0f;
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float f = sm_m[w][g] == kNegInf ? 0.0f : fast_exp2(sm_m[w][g] - M);
       lsum += f * sm_l[w][g];
-      o += f * sm_acc[w][g][d];
+      const f4_t x = *reinterpret_cast<const f4_t*>(&sm_acc[w][g][d]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += f * x[e];
     }
     const bool any = lsum > 0.0f;
     const int h = sg.h0 + g;
     const int64_t row = ((int64_t)sg.b * a.heads + h) * ns + sg.sid;  // [B, H, ns]
-    if (a.direct) {
-      store_out<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, any ? o / lsum : 0.0f);
-    } else if (a.unnorm) {
-      a.opart[row * D + d] = o;
+    if (a.unnorm && !a.direct) {
+      *reinterpret_cast<f4_t*>(a.opart + row * D + d) = f4_t{o[0], o[1], o[2], o[3]};
       if (d == 0) {
         a.mbuf[row] = M;  // -inf for an empty split
         a.lbuf[row] = lsum;
       }
+      continue;
+    }
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = any ? o[e] / lsum : 0.0f;
+    if (a.direct) {
+      store_out4<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, r);
     } else {
-      a.opart[row * D + d] = any ? o / lsum : 0.0f;
+      *reinterpret_cast<f4_t*>(a.opart + row * D + d) = f4_t{r[0], r[1], r[2], r[3]};
       if (d == 0)
         a.lse[((int64_t)sg.b * ns + sg.sid) * a.heads + h] = any ? fast_log2(lsum) + M : kNegInf;
     }
@@ -423,7 +483,7 @@ __device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF 
 
 // --------------------------------------------------------- VALU kernel --
 template <int DT, int D, int GC, bool NT, int NW>
-__global__ __launch_bounds__(kWave* NW) void split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kWave* NW) void split_kernel(const int32_t* cu, int batch, SplitArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int EPL = 16 / EB;         // elements per 16-byte chunk
   constexpr int LPR = D / EPL;         // lanes per K/V row
@@ -440,7 +500,8 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(SplitArgs a) {
   const int rg = lane / LPR;  // which row of a load this lane holds
   const int c = lane % LPR;   // which 16-byte chunk of the row
 
-  const LaneSeqs ls = lane_seqs(a);
+  const SeqTable st{cu, batch};
+  const LaneSeqs ls = lane_seqs(st);
   // q chunks of the packed rows of the current item (rows past the group
   // read as zero)
   u4_t q[GC];
@@ -547,7 +608,7 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(SplitArgs a) {
   Tile buf[kPrefetchTilesValu + 1];
   const WorkItem wi = decode_item<GC>(a, blockIdx.x);
   load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
-  sg = locate_segment<EB>(a, wi, ls);
+  sg = locate_segment<EB>(a, st, wi, ls);
   if (sg.b != wi.rank) load_q(wi, sg.b);
   load_tile_of(sg, wave, buf[0]);
   if constexpr (DT == DT_F32) {
@@ -582,7 +643,7 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(SplitArgs a) {
   // ---- merge the waves through LDS and write the epilogue ----
   __shared__ float sm_m[NW][GC];
   __shared__ float sm_l[NW][GC];
-  __shared__ float sm_acc[NW][GC][D];
+  __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
   if (rg == 0) {
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
@@ -625,7 +686,6 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>
 __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) {
@@ -638,7 +698,7 @@ __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) 
 }
 
 template <int DT, int GC, bool NT>
-__global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(SplitArgs a) {
+__global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int32_t* cu, int batch, SplitArgs a) {
   static_assert(DT == DT_F16 || DT == DT_BF16, "matrix-core path takes 16-bit inputs");
   static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
   constexpr int D = 128;
@@ -653,7 +713,8 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(SplitArgs
   const int R = lane >> 4;   // key group of this lane
   const int c = lane & 15;   // K row / query row / V chunk of this lane
 
-  const LaneSeqs ls = lane_seqs(a);
+  const SeqTable st{cu, batch};
+  const LaneSeqs ls = lane_seqs(st);
   // Q^T as the MFMA B operand: column c = query row h0 + c of the current
   // item (zero past the group)
   u4_t qb[KS];
@@ -768,7 +829,7 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(SplitArgs
   Tile buf[kPrefetchTilesMfma + 1];
   const WorkItem wi = decode_item<GC>(a, blockIdx.x);
   load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
-  sg = locate_segment<EB>(a, wi, ls);
+  sg = locate_segment<EB>(a, st, wi, ls);
   if (sg.b != wi.rank) load_q(wi, sg.b);
   load_tile_of(sg, wave, buf[0]);
   m_run = kNegInf;
@@ -785,26 +846,34 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(SplitArgs
   const float M = across_groups<16>(m_true, OpMax{});
   const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
   const float lw = across_groups<16>(l_run * f, OpAdd{});
+  // value v = 8g + e (query row g, dim 8c + e of this lane), scaled onto M,
+  // then summed over the four rows R by a reduce-scatter: lane (R, c) ends
+  // with the wave's total of value 4j + R, i.e. row g = j / 2, dim
+  // 8c + 4 (j % 2) + R.
+  constexpr int NV = GC * 8;
+  float x[NV];
   static_for<GC>([&](auto gi) {
     constexpr int g = decltype(gi)::value;
     const float fg = row_bcast<g>(f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = across_groups<16>(acc[g][e] * fg, OpAdd{});
+    for (int e = 0; e < 8; ++e) x[8 * g + e] = acc[g][e] * fg;
   });
+  float s2[NV / 2];
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) s2[i] = rows_scatter(x[2 * i], x[2 * i + 1]);
+  float s4[NV / 4];
+#pragma unroll
+  for (int j = 0; j < NV / 4; ++j) s4[j] = halves_scatter(s2[2 * j], s2[2 * j + 1]);
 
   // ---- merge the waves through LDS and write the epilogue ----
   __shared__ float sm_m[NW][GC];
   __shared__ float sm_l[NW][GC];
-  __shared__ float sm_acc[NW][GC][D];
-  if (R == 0) {
+  __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
 #pragma unroll
-    for (int g = 0; g < GC; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][g][8 * c + e] = acc[g][e];
-    if (c < GC) {
-      sm_m[wave][c] = M;
-      sm_l[wave][c] = lw;
-    }
+  for (int j = 0; j < NV / 4; ++j) sm_acc[wave][j / 2][8 * c + 4 * (j % 2) + R] = s4[j];
+  if (R == 0 && c < GC) {
+    sm_m[wave][c] = M;
+    sm_l[wave][c] = lw;
   }
   __syncthreads();
   store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
@@ -855,7 +924,7 @@ hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, h
 #define FD_CASE(R)                                                                        \
   case R:                                                                                 \
     hipLaunchKernelGGL((split_kernel_mfma<DT, R, NT>), grid, block,                       \
-                       (mfma_lds_reserve<DT, R, NT>()), s, a);                            \
+                       (mfma_lds_reserve<DT, R, NT>()), s, a.cu, a.batch, a);             \
     break;
         FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
 #undef FD_CASE
@@ -870,7 +939,8 @@ hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, h
       switch (rows) {
 #define FD_CASE(R)                                                                            \
   case R:                                                                                     \
-    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValuWide>), grid, block, 0, s, a); \
+    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValuWide>), grid, block, 0, s, a.cu, \
+                       a.batch, a);                                                          \
     break;
         FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
 #undef FD_CASE
@@ -882,7 +952,10 @@ hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, h
   const dim3 block(kWave * kWavesValu);
   switch (rows) {
 #define FD_CASE(R) \
-  case R: hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValu>), grid, block, 0, s, a); break;
+  case R:                                                                                        \
+    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValu>), grid, block, 0, s, a.cu, a.batch, \
+                       a);                                                                     \
+    break;
     FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
 #undef FD_CASE
     default: return hipErrorInvalidValue;
