@@ -181,9 +181,13 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     B, Hq, D = w.batch, w.heads, w.dim
     unnorm = fmt == "unnorm"
     ws_bytes = (fd.fd_workspace_bytes_unnorm if unnorm else fd.fd_workspace_bytes)(B, Hq, ns, D)
-    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    # zero-filled once: the arrival counters of fused calls start at zero
+    ws = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    single_launch = ns == 1
+    mode = fd.fd_set_combine(fd.FD_COMBINE_SEPARATE)
+    fd.fd_set_combine(mode)
+    # one launch per call: a single split, or the fused combine (normalised format)
+    single_launch = ns == 1 or (mode == fd.FD_COMBINE_FUSED and not unnorm)
     attention = fd.fd_decode_attention_unnorm if unnorm else fd.fd_decode_attention
     split = fd.fd_decode_split_unnorm if unnorm else fd.fd_decode_split
 
@@ -324,6 +328,13 @@ def main():
                     default="auto",
                     help="split kernel variant (default: the library's own choice; "
                          "unpacked = one query head per workgroup, the comparison path)")
+    ap.add_argument("--schedule", choices=["auto", "static", "queue"], default="auto",
+                    help="how split launches hand segments to workgroups (default: the "
+                         "library's choice; queue = a device-sized grid claiming segments "
+                         "from a counter)")
+    ap.add_argument("--combine", choices=["separate", "fused"], default="separate",
+                    help="merge the partials in the combine kernel (default) or in the split "
+                         "kernel's last workgroup per (sequence, KV head): one launch")
     ap.add_argument("--format", choices=["lse", "unnorm"], default="lse",
                     help="split format: normalised partials + LSE with proportional bounds "
                          "(default), or (m, l, acc) with ceil-equal bounds")
@@ -348,6 +359,9 @@ def main():
     fd.fd_set_kernel_path({"auto": fd.FD_PATH_AUTO, "valu": fd.FD_PATH_VALU,
                            "mfma": fd.FD_PATH_MFMA,
                            "unpacked": fd.FD_PATH_UNPACKED}[args.kernel_path])
+    fd.fd_set_schedule({"auto": fd.FD_SCHED_AUTO, "static": fd.FD_SCHED_STATIC,
+                        "queue": fd.FD_SCHED_QUEUE}[args.schedule])
+    fd.fd_set_combine(fd.FD_COMBINE_FUSED if args.combine == "fused" else fd.FD_COMBINE_SEPARATE)
     rows = 1 if args.kernel_path == "unpacked" else 8
     if args.all or args.sweep_splits:
         import torch
@@ -363,6 +377,8 @@ def main():
             r = run(w, args.steps, args.warmup, cpu_s, ns_override=ns, rows_per_workgroup=rows,
                     fmt=args.format, graph=args.graph)
             r["kernel_path"] = args.kernel_path
+            r["schedule"] = args.schedule
+            r["combine"] = args.combine
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
         return
@@ -371,6 +387,8 @@ def main():
             ns_override=args.num_splits, rows_per_workgroup=rows, fmt=args.format,
             graph=args.graph)
     r["kernel_path"] = args.kernel_path
+    r["schedule"] = args.schedule
+    r["combine"] = args.combine
     print(json.dumps(r), flush=True)
 
 

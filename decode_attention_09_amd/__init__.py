@@ -19,13 +19,16 @@ __all__ = [
     "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "FD_PATH_UNPACKED", "workspace_views",
     "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
     "fd_decode_attention_unnorm", "workspace_views_unnorm", "fd_decode_attention_noalloc",
-    "FD_NOALLOC_SCRATCH_BYTES",
+    "FD_NOALLOC_SCRATCH_BYTES", "fd_set_schedule", "FD_SCHED_AUTO", "FD_SCHED_STATIC",
+    "FD_SCHED_QUEUE", "fd_set_combine", "FD_COMBINE_SEPARATE", "FD_COMBINE_FUSED",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_MAX_SPLITS = 16384
 FD_NOALLOC_SCRATCH_BYTES = 16 << 20
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA, FD_PATH_UNPACKED = 0, 1, 2, 3
+FD_SCHED_AUTO, FD_SCHED_STATIC, FD_SCHED_QUEUE = 0, 1, 2
+FD_COMBINE_SEPARATE, FD_COMBINE_FUSED = 0, 1
 _STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
            3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP", 5: "FD_ERR_SCRATCH"}
 
@@ -97,6 +100,10 @@ def load_library():
     lib.fd_last_error.restype = ctypes.c_char_p
     lib.fd_set_kernel_path.argtypes = [i32]
     lib.fd_set_kernel_path.restype = i32
+    lib.fd_set_schedule.argtypes = [i32]
+    lib.fd_set_schedule.restype = i32
+    lib.fd_set_combine.argtypes = [i32]
+    lib.fd_set_combine.restype = i32
     _LIB = lib
     return lib
 
@@ -120,6 +127,29 @@ def fd_set_kernel_path(path: int) -> int:
     prev = load_library().fd_set_kernel_path(int(path))
     if prev < 0:
         raise ValueError(f"unknown kernel path {path}")
+    return prev
+
+
+def fd_set_schedule(sched: int) -> int:
+    """Select how split launches from this thread hand segments to
+    workgroups (FD_SCHED_AUTO / _STATIC / _QUEUE); returns the previous
+    setting. The results are bitwise identical under every schedule."""
+    prev = load_library().fd_set_schedule(int(sched))
+    if prev < 0:
+        raise ValueError(f"unknown schedule {sched}")
+    return prev
+
+
+def fd_set_combine(mode: int) -> int:
+    """Select where fd_decode_attention calls from this thread merge the
+    partials (FD_COMBINE_SEPARATE: the combine kernel; FD_COMBINE_FUSED: the
+    last split workgroup of each (sequence, KV head), one launch); returns
+    the previous setting. A fused call needs the workspace's arrival counters
+    at zero: workspaces this binding allocates are zero-filled, and a caller's
+    own workspace must be zeroed once when allocated."""
+    prev = load_library().fd_set_combine(int(mode))
+    if prev < 0:
+        raise ValueError(f"unknown combine mode {mode}")
     return prev
 
 
@@ -238,7 +268,8 @@ def _workspace(q, batch, heads, dim, num_splits, workspace, unnorm=False):
     size = fd_workspace_bytes_unnorm if unnorm else fd_workspace_bytes
     need = size(batch, heads, num_splits, dim)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: the arrival counters of a fused call must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace too small: need {need} bytes")
     return workspace

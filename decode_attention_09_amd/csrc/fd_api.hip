@@ -34,6 +34,10 @@ thread_local char g_last_error[256] = "";
 // Split-kernel choice of fd_set_kernel_path: per thread, so callers on
 // different threads never steer each other's launches.
 thread_local int g_path = FD_PATH_AUTO;
+// Schedule of the split launch (fd_set_schedule) and where whole calls
+// merge the partials (fd_set_combine), per thread like the path.
+thread_local int g_sched = FD_SCHED_AUTO;
+thread_local int g_combine = FD_COMBINE_SEPARATE;
 
 // The library's own choice of split kernel: matrix-core QK^T wherever that
 // kernel exists (16-bit inputs, head dim 128) and the group has at least 2
@@ -176,7 +180,12 @@ int check_layout(const fd_kv_layout* lay, int kv_heads, int dim, int dtype, fd_k
 
 // The two workspace formats.
 //   kNormalised: Opart [B,H,ns,D] o_s, then (256-B aligned) LSE [B,ns,H]
-//                (decode_attention_splitkv.py's part_shape / lse_shape).
+//                (decode_attention_splitkv.py's part_shape / lse_shape),
+//                then (256-B aligned) the control block: the claim counter
+//                of a queue-scheduled launch (first int32 of 256 bytes),
+//                then int32 arrival counters [B*H] of fused calls (256-B
+//                aligned size), which must be zero before a fused call and
+//                are left zero by it.
 //   kUnnorm:     ACC [B,H,ns,D] acc_s, then (256-B aligned) M [B,H,ns],
 //                then (256-B aligned) L [B,H,ns] (flash_decode_splitk.py's
 //                ACC_BUF, M_BUF, L_BUF), with ceil-equal split bounds.
@@ -189,12 +198,21 @@ struct Workspace {
   float* lse = nullptr;
   float* mbuf = nullptr;
   float* lbuf = nullptr;
+  int* queue = nullptr;     // claim counter (normalised format)
+  int* arrivals = nullptr;  // arrival counters of fused calls (normalised format)
 };
+
+constexpr size_t kQueueBytes = 256;
+
+size_t control_bytes(int batch, int heads) {
+  return kQueueBytes + align256((size_t)batch * heads * sizeof(int));
+}
 
 size_t workspace_bytes(Format f, int batch, int heads, int dim, int num_splits) {
   const size_t rows = (size_t)batch * heads * num_splits;
   const size_t opart = align256(rows * dim * sizeof(float));
-  if (f == kNormalised) return opart + rows * sizeof(float);
+  if (f == kNormalised)
+    return opart + align256(rows * sizeof(float)) + control_bytes(batch, heads);
   return opart + align256(rows * sizeof(float)) + rows * sizeof(float);
 }
 
@@ -206,6 +224,8 @@ Workspace workspace_views(Format f, void* base, int batch, int heads, int dim, i
   w.opart = reinterpret_cast<float*>(ws);
   if (f == kNormalised) {
     w.lse = reinterpret_cast<float*>(ws + opart);
+    w.queue = reinterpret_cast<int*>(ws + opart + align256(rows * sizeof(float)));
+    w.arrivals = reinterpret_cast<int*>(ws + opart + align256(rows * sizeof(float)) + kQueueBytes);
   } else {
     w.mbuf = reinterpret_cast<float*>(ws + opart);
     w.lbuf = reinterpret_cast<float*>(ws + opart + align256(rows * sizeof(float)));
@@ -213,10 +233,22 @@ Workspace workspace_views(Format f, void* base, int batch, int heads, int dim, i
   return w;
 }
 
+// FD_SCHED_AUTO keeps the static schedule. Measured on MI355X (same split
+// count, A/B in one process), the queue schedule with one workgroup per
+// compute unit wins only on ragged batches: varlen Qwen (32 sequences of
+// 64..32768 keys, 8 splits) 201.9 -> 187.2 us; it loses on uniform lengths,
+// where each extra segment a workgroup walks exposes its fixed costs
+// (Llama B16/8K +2.5 % at 8 splits, +9 % at 16; flash-decoding B64/2K
+// +24 %, B8/8K at 64 splits +32 %; MHA +19..49 %). The lengths are on the
+// device, so the host cannot tell the cases apart: callers with ragged
+// batches select FD_SCHED_QUEUE.
+bool use_queue(int sched) { return sched == FD_SCHED_QUEUE; }
+
 int launch_split(const void* q, const void* k, const void* v, const int32_t* cu, int batch,
                  int heads, int kv_heads, int dim, int num_splits, float scale, Format fmt,
                  const Workspace& w, void* out, int direct, hipStream_t stream, int dtype,
-                 const fd_kv_layout& L, const Sizes& sz, int path) {
+                 const fd_kv_layout& L, const Sizes& sz, int path, int sched,
+                 bool fused = false) {
   fd::SplitArgs a;
   a.q = q;
   a.k = k;
@@ -251,6 +283,16 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   if (cst != FD_OK) return cst;
   a.kv_nt = path != FD_PATH_UNPACKED && sz.workgroups >= cus ? 1 : 0;
   a.wide = sz.workgroups < cus ? 1 : 0;
+  a.cus = cus;
+  a.items = (int)sz.workgroups;
+  // (queued launches fill the device, so they always take non-temporal loads)
+  a.arrivals = fused ? w.arrivals : nullptr;
+  a.queue = !fused && w.queue != nullptr && a.kv_nt && use_queue(sched) ? w.queue
+                                                                                   : nullptr;
+  if (a.queue != nullptr) {
+    const hipError_t er = fd::launch_queue_reset(a.queue, stream);
+    if (er != hipSuccess) return hip_fail(er, "queue reset launch");
+  }
   dim3 grid((unsigned)sz.workgroups);
   const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;
@@ -280,7 +322,8 @@ int split_impl(Format fmt, const void* q, const void* k, const void* v,
   if (st != FD_OK) return st;
   const Workspace w = workspace_views(fmt, workspace, batch, heads, dim, num_splits);
   return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale, fmt,
-                      w, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path);
+                      w, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path,
+                      g_sched);
 }
 
 int combine_impl(Format fmt, const void* workspace, int batch, int heads, int dim,
@@ -324,7 +367,7 @@ int check_attention(const void* q, const void* k, const void* v, const int32_t* 
 int attention_impl(Format fmt, const void* q, const void* k, const void* v,
                    const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
                    int num_splits, float scale, void* out, void* workspace, void* stream,
-                   int dtype, const fd_kv_layout* layout) {
+                   int dtype, const fd_kv_layout* layout, int combine) {
   const int path = g_path;
   Sizes sz;
   fd_kv_layout L;
@@ -336,8 +379,17 @@ int attention_impl(Format fmt, const void* q, const void* k, const void* v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (num_splits == 1) {
     // one split is the whole sequence under either bound rule: one launch
-    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, fmt,
-                        Workspace{}, out, 1, s, dtype, L, sz, path);
+    Workspace w;
+    if (workspace != nullptr && fmt == kNormalised)
+      w.queue = workspace_views(fmt, workspace, batch, heads, dim, 1).queue;
+    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, 1, scale, fmt, w, out,
+                        1, s, dtype, L, sz, path, g_sched);
+  }
+  if (fmt == kNormalised && combine == FD_COMBINE_FUSED) {
+    // one launch: the split kernel's last workgroup per unit merges
+    const Workspace w = workspace_views(fmt, workspace, batch, heads, dim, num_splits);
+    return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
+                        fmt, w, out, 0, s, dtype, L, sz, path, FD_SCHED_STATIC, true);
   }
   st = split_impl(fmt, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
                   workspace, stream, dtype, layout);
@@ -444,7 +496,7 @@ int fd_decode_attention(const void* q, const void* k, const void* v, const int32
                         void* out, void* workspace, void* stream, int dtype,
                         const fd_kv_layout* layout) {
   return attention_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim,
-                        num_splits, scale, out, workspace, stream, dtype, layout);
+                        num_splits, scale, out, workspace, stream, dtype, layout, g_combine);
 }
 
 int fd_decode_split_unnorm(const void* q, const void* k, const void* v,
@@ -465,7 +517,7 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
                                int dim, int num_splits, float scale, void* out, void* workspace,
                                void* stream, int dtype, const fd_kv_layout* layout) {
   return attention_impl(kUnnorm, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
-                        scale, out, workspace, stream, dtype, layout);
+                        scale, out, workspace, stream, dtype, layout, FD_COMBINE_SEPARATE);
 }
 
 int fd_decode_attention_noalloc(const void* q, const void* k, const void* v,
@@ -489,8 +541,10 @@ int fd_decode_attention_noalloc(const void* q, const void* k, const void* v,
     const int s2 = scratch_on_device(&ws);
     if (s2 != FD_OK) return s2;
   }
+  // the scratch's arrival counters would move with the call's sizes, over
+  // earlier calls' partials, so these calls always merge in the combine kernel
   return attention_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim,
-                        num_splits, scale, out, ws, stream, dtype, layout);
+                        num_splits, scale, out, ws, stream, dtype, layout, FD_COMBINE_SEPARATE);
 }
 
 const char* fd_status_string(int status) {
@@ -506,6 +560,20 @@ const char* fd_status_string(int status) {
 }
 
 const char* fd_last_error(void) { return g_last_error; }
+
+int fd_set_combine(int mode) {
+  if (mode != FD_COMBINE_SEPARATE && mode != FD_COMBINE_FUSED) return -1;
+  const int prev = g_combine;
+  g_combine = mode;
+  return prev;
+}
+
+int fd_set_schedule(int sched) {
+  if (sched != FD_SCHED_AUTO && sched != FD_SCHED_STATIC && sched != FD_SCHED_QUEUE) return -1;
+  const int prev = g_sched;
+  g_sched = sched;
+  return prev;
+}
 
 int fd_set_kernel_path(int path) {
   if (path != FD_PATH_AUTO && path != FD_PATH_VALU && path != FD_PATH_MFMA &&

@@ -205,6 +205,19 @@ static hipError_t launch_combine_dt(const CombineArgs& a, int dim, hipStream_t s
   return hipGetLastError();
 }
 
+// One thread zeroes the claim counter of the queue-scheduled split launch
+// that follows on the same stream (stream order makes the zero visible to
+// it). A kernel rather than a memset, so that a captured graph holds no
+// memset node.
+__global__ void queue_reset_kernel(int* queue) {
+  if (threadIdx.x == 0) queue[0] = 0;
+}
+
+hipError_t launch_queue_reset(int* queue, hipStream_t s) {
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, s, queue);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s) {
   switch (dtype) {
     case DT_F32: return launch_combine_dt<DT_F32>(a, dim, s);

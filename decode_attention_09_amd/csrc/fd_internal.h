@@ -78,6 +78,18 @@ struct SplitArgs {
   int ceil_bounds;  // 1: ceil-equal split bounds; 0: proportional
   int unnorm;       // 1: workspace holds (m, l, acc); 0: (o_s, lse2_s)
   float scale_log2; // scale * log2(e)
+  // Queue schedule: `queue` points at a claim counter that is zero when the
+  // launch starts; workgroup w first takes segment w, then claims segments
+  // gridDim.x, gridDim.x + 1, ... from the counter until `items` is reached.
+  // nullptr: one segment per workgroup (the grid covers every segment).
+  int* queue;
+  int items;
+  int cus;          // compute units of the device (sizes a queue-scheduled grid)
+  // Single launch (fused combine): one arrival counter per (sequence, KV
+  // head, row chunk), zero before the launch; the last of the unit's
+  // num_splits workgroups to arrive merges the unit's partials into `out`
+  // and sets the counter back to zero. nullptr: the combine kernel merges.
+  int* arrivals;
 };
 
 struct CombineArgs {
@@ -101,5 +113,7 @@ hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, bool mfma, di
 hipError_t launch_split_bf16(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
                              hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s);
+// Zeroes the claim counter of a queue-scheduled split launch (one thread).
+hipError_t launch_queue_reset(int* queue, hipStream_t s);
 
 }  // namespace fd

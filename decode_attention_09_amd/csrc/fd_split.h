@@ -431,11 +431,97 @@ __device__ __forceinline__ void store_segment(const SplitArgs& a, const Segment&
     if (a.direct) {
       store_out4<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, r);
     } else {
+      if (a.arrivals != nullptr) {
+        // fused launch: agent-scope (write-through) stores, which the last
+        // workgroup of the unit reads after the release/acquire on the
+        // arrival counter. Measured on MI355X against plain stores (whose
+        // lines the release then writes back from L2): flash-decoding B8/8K
+        // 26.2 -> 21.1 us and B1/64K 37.8 -> 33.2 us per call.
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(a.opart + row * D + d + e, r[e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(a.lse + ((int64_t)sg.b * ns + sg.sid) * a.heads + h,
+                             any ? fast_log2(lsum) + M : kNegInf, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        continue;
+      }
       *reinterpret_cast<f4_t*>(a.opart + row * D + d) = f4_t{r[0], r[1], r[2], r[3]};
       if (d == 0)
         a.lse[((int64_t)sg.b * ns + sg.sid) * a.heads + h] = any ? fast_log2(lsum) + M : kNegInf;
     }
   }
+}
+
+// ------------------------------------------------ single-launch combine --
+// In a fused launch, a workgroup counts itself in at its unit's arrival
+// counter once its partials are stored; the last of the unit's num_splits
+// workgroups merges the unit's partials into `out` -- the combine segment
+// of gqa_decode_splitkv in "decode_attention_splitkv.py" (TileLang tutorial,
+// ch. 18) and the merge of "04_flash_decoding.py" (CS349E lecture 11),
+// demo 1: M = max_s lse_s, lse = M + log2 sum_s 2^(lse_s - M),
+// o = sum_s 2^(lse_s - lse) o_s -- and sets the counter back to zero.
+// Synchronisation follows the HIP memory model at agent scope: the barrier
+// orders every thread's partial stores before thread 0's acq_rel fetch_add,
+// whose release makes them visible to the workgroup that later acquires
+// the counter; that last arriver's fetch_add plus an acquire fence in each
+// of its waves make every other workgroup's partials visible to its loads.
+// All threads of the workgroup call it (it synchronises); `slot` is an LDS
+// int for the broadcast.
+template <int DT, int D, int NW>
+__device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const Segment& sg, int unit,
+                                                 int& slot) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    slot = __hip_atomic_fetch_add(a.arrivals + unit, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (slot != a.num_splits - 1) return;  // uniform: a split of this unit is still running
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  constexpr int Q = D / 4;  // groups of four dims per row, as in store_segment
+  const int ns = a.num_splits;
+  const int64_t kst = a.heads;  // LSE [B, ns, H]: split stride
+  for (int idx = threadIdx.x; idx < sg.nrows * Q; idx += NW * kWave) {
+    const int g = idx / Q;
+    const int d = (idx % Q) * 4;
+    const int h = sg.h0 + g;
+    const float* lse = a.lse + (int64_t)sg.b * ns * a.heads + h;
+    const float* op = a.opart + ((int64_t)sg.b * a.heads + h) * ns * D + d;  // split stride: D
+    float M = kNegInf;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, lse[s * kst]);
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (M != kNegInf) {  // all splits empty -> zero row
+      float tot = 0.0f;
+#pragma unroll 8
+      for (int s = 0; s < ns; ++s) tot += fast_exp2(lse[s * kst] - M);
+      const float lse_all = M + fast_log2(tot);
+#pragma unroll 8
+      for (int s = 0; s < ns; ++s) {
+        const float w = fast_exp2(lse[s * kst] - lse_all);
+        const f4_t x = *reinterpret_cast<const f4_t*>(op + (int64_t)s * D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, x[e], o[e]);
+      }
+    }
+    store_out4<DT>(a.out, ((int64_t)sg.b * a.heads + h) * D + d, o);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.arrivals + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Queue schedule: after a segment, thread 0 claims the next one from the
+// counter (segments below gridDim.x are the workgroups' first ones, taken
+// without a claim). The barrier hands the index to every thread and keeps the
+// next segment's LDS writes behind all reads of this one. A relaxed atomic
+// suffices: the counter passes no data, each value goes to exactly one
+// claim, and the partials are read only by the next launch.
+__device__ __forceinline__ int claim_next(const SplitArgs& a, int& slot) {
+  if (threadIdx.x == 0)
+    slot = (int)gridDim.x +
+           __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return slot;
 }
 
 // ------------------------------------------------------------ pipeline --
@@ -482,7 +568,7 @@ __device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF 
 }
 
 // --------------------------------------------------------- VALU kernel --
-template <int DT, int D, int GC, bool NT, int NW>
+template <int DT, int D, int GC, bool NT, int NW, bool QUEUE>
 __global__ __launch_bounds__(kWave* NW) void split_kernel(const int32_t* cu, int batch, SplitArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int EPL = 16 / EB;         // elements per 16-byte chunk
@@ -606,57 +692,67 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(const int32_t* cu, int
   };
 
   Tile buf[kPrefetchTilesValu + 1];
-  const WorkItem wi = decode_item<GC>(a, blockIdx.x);
-  load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
-  sg = locate_segment<EB>(a, st, wi, ls);
-  if (sg.b != wi.rank) load_q(wi, sg.b);
-  load_tile_of(sg, wave, buf[0]);
-  if constexpr (DT == DT_F32) {
+  __shared__ int sm_next;
+  int item = blockIdx.x;
+  while (true) {
+    const WorkItem wi = decode_item<GC>(a, item);
+    load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
+    sg = locate_segment<EB>(a, st, wi, ls);
+    if (sg.b != wi.rank) load_q(wi, sg.b);
+    load_tile_of(sg, wave, buf[0]);
+    if constexpr (DT == DT_F32) {
 #pragma unroll
-    for (int g = 0; g < GC; ++g)
+      for (int g = 0; g < GC; ++g)
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        q[g][w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, word(q[g], w)) * a.scale_log2);
-  }
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    m[g] = kNegInf;
-    mt[g] = kNegInf;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  }
-  const int nt = (int)((sg.nkeys + TK - 1) / TK);
-  tile_pipeline<kPrefetchTilesValu, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
-
-  // ---- merge the lane groups of this wave onto the wave's true max ----
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const float M = across_groups<LPR>(mt[g], OpMax{});
-    const float f = m[g] == kNegInf ? 0.0f : fast_exp2(m[g] - M);
-    l[g] = across_groups<LPR>(l[g] * f, OpAdd{});
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = across_groups<LPR>(acc[g][e] * f, OpAdd{});
-    m[g] = M;
-  }
-
-  // ---- merge the waves through LDS and write the epilogue ----
-  __shared__ float sm_m[NW][GC];
-  __shared__ float sm_l[NW][GC];
-  __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
-  if (rg == 0) {
+        for (int w = 0; w < 4; ++w)
+          q[g][w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, word(q[g], w)) * a.scale_log2);
+    }
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
+      m[g] = kNegInf;
+      mt[g] = kNegInf;
+      l[g] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][g][c * EPL + e] = acc[g][e];
-      if (c == 0) {
-        sm_m[wave][g] = m[g];
-        sm_l[wave][g] = l[g];
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+    }
+    const int nt = (int)((sg.nkeys + TK - 1) / TK);
+    tile_pipeline<kPrefetchTilesValu, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+
+    // ---- merge the lane groups of this wave onto the wave's true max ----
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      const float M = across_groups<LPR>(mt[g], OpMax{});
+      const float f = m[g] == kNegInf ? 0.0f : fast_exp2(m[g] - M);
+      l[g] = across_groups<LPR>(l[g] * f, OpAdd{});
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = across_groups<LPR>(acc[g][e] * f, OpAdd{});
+      m[g] = M;
+    }
+
+    // ---- merge the waves through LDS and write the epilogue ----
+    __shared__ float sm_m[NW][GC];
+    __shared__ float sm_l[NW][GC];
+    __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
+    if (rg == 0) {
+#pragma unroll
+      for (int g = 0; g < GC; ++g) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_acc[wave][g][c * EPL + e] = acc[g][e];
+        if (c == 0) {
+          sm_m[wave][g] = m[g];
+          sm_l[wave][g] = l[g];
+        }
       }
     }
+    __syncthreads();
+    store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
+    if constexpr (!QUEUE) {  // static schedule: the loop body runs once
+      if (a.arrivals != nullptr) arrive_and_merge<DT, D, NW>(a, sg, item / a.num_splits, sm_next);
+      break;
+    }
+    item = claim_next(a, sm_next);
+    if (item >= a.items) break;
   }
-  __syncthreads();
-  store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
 }
 
 // --------------------------------------------------------- MFMA kernel --
@@ -697,7 +793,7 @@ __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) 
                                                    __builtin_bit_cast(b8_t, q), acc, 0, 0, 0);
 }
 
-template <int DT, int GC, bool NT>
+template <int DT, int GC, bool NT, bool QUEUE>
 __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int32_t* cu, int batch, SplitArgs a) {
   static_assert(DT == DT_F16 || DT == DT_BF16, "matrix-core path takes 16-bit inputs");
   static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
@@ -827,56 +923,66 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
   };
 
   Tile buf[kPrefetchTilesMfma + 1];
-  const WorkItem wi = decode_item<GC>(a, blockIdx.x);
-  load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
-  sg = locate_segment<EB>(a, st, wi, ls);
-  if (sg.b != wi.rank) load_q(wi, sg.b);
-  load_tile_of(sg, wave, buf[0]);
-  m_run = kNegInf;
-  m_true = kNegInf;
-  l_run = 0.0f;
+  __shared__ int sm_next;
+  int item = blockIdx.x;
+  while (true) {
+    const WorkItem wi = decode_item<GC>(a, item);
+    load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
+    sg = locate_segment<EB>(a, st, wi, ls);
+    if (sg.b != wi.rank) load_q(wi, sg.b);
+    load_tile_of(sg, wave, buf[0]);
+    m_run = kNegInf;
+    m_true = kNegInf;
+    l_run = 0.0f;
 #pragma unroll
-  for (int g = 0; g < GC; ++g)
+    for (int g = 0; g < GC; ++g)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
-  const int nt = (int)((sg.nkeys + TK - 1) / TK);
-  tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+      for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+    const int nt = (int)((sg.nkeys + TK - 1) / TK);
+    tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
 
-  // ---- merge the four key groups R of this wave onto its true max ----
-  const float M = across_groups<16>(m_true, OpMax{});
-  const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
-  const float lw = across_groups<16>(l_run * f, OpAdd{});
-  // value v = 8g + e (query row g, dim 8c + e of this lane), scaled onto M,
-  // then summed over the four rows R by a reduce-scatter: lane (R, c) ends
-  // with the wave's total of value 4j + R, i.e. row g = j / 2, dim
-  // 8c + 4 (j % 2) + R.
-  constexpr int NV = GC * 8;
-  float x[NV];
-  static_for<GC>([&](auto gi) {
-    constexpr int g = decltype(gi)::value;
-    const float fg = row_bcast<g>(f);
+    // ---- merge the four key groups R of this wave onto its true max ----
+    const float M = across_groups<16>(m_true, OpMax{});
+    const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+    const float lw = across_groups<16>(l_run * f, OpAdd{});
+    // value v = 8g + e (query row g, dim 8c + e of this lane), scaled onto M,
+    // then summed over the four rows R by a reduce-scatter: lane (R, c) ends
+    // with the wave's total of value 4j + R, i.e. row g = j / 2, dim
+    // 8c + 4 (j % 2) + R.
+    constexpr int NV = GC * 8;
+    float x[NV];
+    static_for<GC>([&](auto gi) {
+      constexpr int g = decltype(gi)::value;
+      const float fg = row_bcast<g>(f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[8 * g + e] = acc[g][e] * fg;
-  });
-  float s2[NV / 2];
+      for (int e = 0; e < 8; ++e) x[8 * g + e] = acc[g][e] * fg;
+    });
+    float s2[NV / 2];
 #pragma unroll
-  for (int i = 0; i < NV / 2; ++i) s2[i] = rows_scatter(x[2 * i], x[2 * i + 1]);
-  float s4[NV / 4];
+    for (int i = 0; i < NV / 2; ++i) s2[i] = rows_scatter(x[2 * i], x[2 * i + 1]);
+    float s4[NV / 4];
 #pragma unroll
-  for (int j = 0; j < NV / 4; ++j) s4[j] = halves_scatter(s2[2 * j], s2[2 * j + 1]);
+    for (int j = 0; j < NV / 4; ++j) s4[j] = halves_scatter(s2[2 * j], s2[2 * j + 1]);
 
-  // ---- merge the waves through LDS and write the epilogue ----
-  __shared__ float sm_m[NW][GC];
-  __shared__ float sm_l[NW][GC];
-  __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
+    // ---- merge the waves through LDS and write the epilogue ----
+    __shared__ float sm_m[NW][GC];
+    __shared__ float sm_l[NW][GC];
+    __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
 #pragma unroll
-  for (int j = 0; j < NV / 4; ++j) sm_acc[wave][j / 2][8 * c + 4 * (j % 2) + R] = s4[j];
-  if (R == 0 && c < GC) {
-    sm_m[wave][c] = M;
-    sm_l[wave][c] = lw;
+    for (int j = 0; j < NV / 4; ++j) sm_acc[wave][j / 2][8 * c + 4 * (j % 2) + R] = s4[j];
+    if (R == 0 && c < GC) {
+      sm_m[wave][c] = M;
+      sm_l[wave][c] = lw;
+    }
+    __syncthreads();
+    store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
+    if constexpr (!QUEUE) {  // static schedule: the loop body runs once
+      if (a.arrivals != nullptr) arrive_and_merge<DT, D, NW>(a, sg, item / a.num_splits, sm_next);
+      break;
+    }
+    item = claim_next(a, sm_next);
+    if (item >= a.items) break;
   }
-  __syncthreads();
-  store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
 }
 
 // Host-side dispatch over (path, D, rows) for one dtype. The matrix-core
@@ -890,12 +996,12 @@ constexpr bool has_mfma_path(int dim) {
 // kMfmaWorkgroupsPerCu matrix-core workgroups reside on one compute unit
 // (0 if the device's per-workgroup limit does not allow it). Computed once
 // per kernel instance.
-template <int DT, int GC, bool NT>
+template <int DT, int GC, bool NT, bool QUEUE>
 size_t mfma_lds_reserve() {
   static const size_t bytes = [] {
     hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&split_kernel_mfma<DT, GC, NT>)) !=
-        hipSuccess) {
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
+                                      &split_kernel_mfma<DT, GC, NT, QUEUE>)) != hipSuccess) {
       (void)hipGetLastError();
       return (size_t)0;
     }
@@ -915,58 +1021,109 @@ size_t mfma_lds_reserve() {
   return bytes;
 }
 
-template <int DT, int D, bool NT>
-hipError_t launch_split_dn(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
-  if constexpr (DT != DT_F32 && D == 128) {
-    if (mfma) {
-      const dim3 block(kWave * kWavesMfma);
-      switch (rows) {
-#define FD_CASE(R)                                                                        \
-  case R:                                                                                 \
-    hipLaunchKernelGGL((split_kernel_mfma<DT, R, NT>), grid, block,                       \
-                       (mfma_lds_reserve<DT, R, NT>()), s, a.cu, a.batch, a);             \
-    break;
-        FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
-#undef FD_CASE
-        default: return hipErrorInvalidValue;
-      }
-      return hipGetLastError();
+#ifndef FD_QUEUE_PER_CU
+#define FD_QUEUE_PER_CU 1
+#endif
+// Workgroups per compute unit of a queue-scheduled launch (0: as many as
+// fit, i.e. the kernel's occupancy). Measured on MI355X (varlen Qwen batch,
+// 8 splits, 1024 segments): one per compute unit 184.7 us, two (the
+// matrix-core kernel's occupancy) 198.2 us, static schedule 195.1 us: a
+// second resident workgroup doubles the bytes in flight per compute unit,
+// which streams slower, as in the static launches.
+constexpr int kQueueWorkgroupsPerCu = FD_QUEUE_PER_CU;
+
+// Grid of a queue-scheduled launch: kQueueWorkgroupsPerCu (at most this
+// kernel's occupancy) workgroups per compute unit, never more than the
+// segments. Computed once per kernel instance.
+template <typename Tag>
+dim3 queue_grid(const SplitArgs& a, const void* kernel, int block, size_t lds) {
+  static const int per_cu = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds) != hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      n = 1;
     }
-  }
-  if constexpr (!NT) {  // launches below one pass never take non-temporal loads
-    if (a.wide) {
-      const dim3 block(kWave * kWavesValuWide);
-      switch (rows) {
-#define FD_CASE(R)                                                                            \
-  case R:                                                                                     \
-    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValuWide>), grid, block, 0, s, a.cu, \
-                       a.batch, a);                                                          \
-    break;
-        FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
-#undef FD_CASE
-        default: return hipErrorInvalidValue;
-      }
-      return hipGetLastError();
-    }
-  }
-  const dim3 block(kWave * kWavesValu);
-  switch (rows) {
-#define FD_CASE(R) \
-  case R:                                                                                        \
-    hipLaunchKernelGGL((split_kernel<DT, D, R, NT, kWavesValu>), grid, block, 0, s, a.cu, a.batch, \
-                       a);                                                                     \
-    break;
-    FD_CASE(1) FD_CASE(2) FD_CASE(3) FD_CASE(4) FD_CASE(5) FD_CASE(6) FD_CASE(7) FD_CASE(8)
-#undef FD_CASE
-    default: return hipErrorInvalidValue;
-  }
+    return kQueueWorkgroupsPerCu > 0 && kQueueWorkgroupsPerCu < n ? kQueueWorkgroupsPerCu : n;
+  }();
+  const long g = (long)per_cu * (a.cus > 0 ? a.cus : 1);
+  return dim3((unsigned)(g < (long)a.items ? g : (long)a.items));
+}
+
+template <int DT, int GC, bool NT, bool QUEUE>
+struct MfmaTag {};
+template <int DT, int D, int GC, bool NT, int NW, bool QUEUE>
+struct ValuTag {};
+
+template <int DT, int GC, bool NT, bool QUEUE>
+hipError_t launch_mfma(const SplitArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(kWave * kWavesMfma);
+  const size_t lds = mfma_lds_reserve<DT, GC, NT, QUEUE>();
+  if constexpr (QUEUE)
+    grid = queue_grid<MfmaTag<DT, GC, NT, QUEUE>>(
+        a, reinterpret_cast<const void*>(&split_kernel_mfma<DT, GC, NT, QUEUE>), block.x, lds);
+  hipLaunchKernelGGL((split_kernel_mfma<DT, GC, NT, QUEUE>), grid, block, lds, s, a.cu, a.batch,
+                     a);
   return hipGetLastError();
 }
 
+template <int DT, int D, int GC, bool NT, int NW, bool QUEUE>
+hipError_t launch_valu(const SplitArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(kWave * NW);
+  if constexpr (QUEUE)
+    grid = queue_grid<ValuTag<DT, D, GC, NT, NW, QUEUE>>(
+        a, reinterpret_cast<const void*>(&split_kernel<DT, D, GC, NT, NW, QUEUE>), block.x, 0);
+  hipLaunchKernelGGL((split_kernel<DT, D, GC, NT, NW, QUEUE>), grid, block, 0, s, a.cu, a.batch,
+                     a);
+  return hipGetLastError();
+}
+
+// f(std::integral_constant<int, rows>) for rows in 1..kMaxRowsPerPass.
+template <typename F>
+hipError_t by_rows(int rows, F&& f) {
+  switch (rows) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Host-side dispatch over (path, D, rows) for one dtype. The matrix-core
+// kernel exists for 16-bit inputs at head dim 128; launches below one pass
+// (never non-temporal, never queued) take 8-wave VALU workgroups.
+template <int DT, int D, bool NT, bool QUEUE>
+hipError_t launch_split_dnq(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
+  if constexpr (DT != DT_F32 && D == 128) {
+    if (mfma)
+      return by_rows(rows, [&](auto r) {
+        return launch_mfma<DT, decltype(r)::value, NT, QUEUE>(a, grid, s);
+      });
+  }
+  if constexpr (!NT && !QUEUE) {
+    if (a.wide)
+      return by_rows(rows, [&](auto r) {
+        return launch_valu<DT, D, decltype(r)::value, NT, kWavesValuWide, QUEUE>(a, grid, s);
+      });
+  }
+  return by_rows(rows, [&](auto r) {
+    return launch_valu<DT, D, decltype(r)::value, NT, kWavesValu, QUEUE>(a, grid, s);
+  });
+}
+
+// The queue schedule is only taken by launches that fill the device (which
+// always carry non-temporal K/V loads); the host never asks for it elsewhere.
 template <int DT, int D>
 hipError_t launch_split_d(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
-  return a.kv_nt ? launch_split_dn<DT, D, true>(a, rows, mfma, grid, s)
-                 : launch_split_dn<DT, D, false>(a, rows, mfma, grid, s);
+  if (a.queue != nullptr && a.kv_nt)
+    return launch_split_dnq<DT, D, true, true>(a, rows, mfma, grid, s);
+  return a.kv_nt ? launch_split_dnq<DT, D, true, false>(a, rows, mfma, grid, s)
+                 : launch_split_dnq<DT, D, false, false>(a, rows, mfma, grid, s);
 }
 
 template <int DT>

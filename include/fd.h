@@ -128,14 +128,22 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
                    int* num_splits_out);
 
 /*
- * fd_workspace_bytes -- size of the fp32 workspace for a call with these
- * sizes (0 on overflow or bad sizes). Layout, all fp32:
- *   Opart [batch, heads, num_splits, dim]  normalised partial outputs o_s
- *   LSE   [batch, num_splits, heads]       log2(sum_t 2^(s2_t)) of split s,
- *                                           s2_t = scale*log2(e)*q.k_t
- * LSE starts at the first 256-byte boundary after Opart. The shapes follow
- * part_shape / lse_shape of decode_attention_splitkv.py, in fp32. Its
- * contents before a call do not matter.
+ * fd_workspace_bytes -- size of the workspace for a call with these
+ * sizes (0 on overflow or bad sizes). Layout:
+ *   Opart [batch, heads, num_splits, dim]  fp32, normalised partial outputs o_s
+ *   LSE   [batch, num_splits, heads]       fp32, log2(sum_t 2^(s2_t)) of split
+ *                                           s, s2_t = scale*log2(e)*q.k_t
+ *   control                                256 bytes holding the claim counter
+ *                                           of a queue-scheduled launch
+ *                                           (fd_set_schedule), then int32
+ *                                           [batch*heads] arrival counters of
+ *                                           fused calls (fd_set_combine),
+ *                                           padded to a multiple of 256 bytes
+ * LSE starts at the first 256-byte boundary after Opart, the control block
+ * at the first 256-byte boundary after LSE. The shapes follow part_shape /
+ * lse_shape of decode_attention_splitkv.py, in fp32. Its contents before a
+ * call do not matter, except for the arrival counters of a fused call,
+ * which must be zero (a queue-scheduled call zeroes its own counter).
  */
 size_t fd_workspace_bytes(int batch, int heads, int num_splits, int dim);
 
@@ -254,6 +262,49 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
  */
 enum { FD_PATH_AUTO = 0, FD_PATH_VALU = 1, FD_PATH_MFMA = 2, FD_PATH_UNPACKED = 3 };
 int fd_set_kernel_path(int path);
+
+/*
+ * fd_set_schedule -- how later split launches from the calling thread hand
+ * segments to workgroups (a per-thread setting, like fd_set_kernel_path).
+ * FD_SCHED_STATIC: one workgroup per segment, in the fixed order of the
+ * grid. FD_SCHED_QUEUE: as many workgroups as the device holds at once;
+ * each takes one segment, then claims the next unprocessed one from a
+ * counter in the workspace's control block (zeroed by a one-thread kernel
+ * launched just before, on the same stream), so compute units that stream
+ * faster process more segments. FD_SCHED_AUTO (the default): the library's
+ * measured choice. The segments, their bounds and every partial are the
+ * same under all schedules, so the results are bitwise identical; the
+ * queue applies to launches with a normalised-format workspace
+ * (fd_decode_attention with a workspace, fd_decode_attention_noalloc,
+ * fd_decode_split) and is ignored elsewhere. Returns the previous
+ * setting, or -1 (unchanged) for an unknown value.
+ */
+enum { FD_SCHED_AUTO = 0, FD_SCHED_STATIC = 1, FD_SCHED_QUEUE = 2 };
+int fd_set_schedule(int sched);
+
+/*
+ * fd_set_combine -- where later fd_decode_attention calls made from the
+ * calling thread merge the partials (a per-thread setting, like
+ * fd_set_kernel_path). FD_COMBINE_SEPARATE (the default): the second
+ * launch, fd_decode_combine's kernel. FD_COMBINE_FUSED: one launch -- the
+ * per-kernel fixed cost that "04_flash_decoding.py" (CS349E lecture 11,
+ * demo 3) counts twice for flash decoding is paid once: each split
+ * workgroup stores its partials and counts itself in at the arrival
+ * counter of its (sequence, KV head) in the workspace's control block (an
+ * agent-scope acq_rel fetch_add); the last of the num_splits workgroups
+ * merges them into `out` with the same LSE formula and sets the counter
+ * back to zero. Requirements of the fused mode: the arrival counters of
+ * the workspace must be zero before the call -- zero the whole workspace
+ * once when it is allocated; every fused call leaves them zero, and
+ * unfused calls never touch them. It applies to fd_decode_attention with
+ * num_splits > 1 (one split is a single launch anyway); the unnormalised
+ * format and fd_decode_attention_noalloc always use the second launch.
+ * Results equal the two-launch path's within the stated tolerances (the
+ * merge sums the splits in a different order). Returns the previous
+ * setting, or -1 (unchanged) for an unknown value.
+ */
+enum { FD_COMBINE_SEPARATE = 0, FD_COMBINE_FUSED = 1 };
+int fd_set_combine(int mode);
 
 /*
  * fd_decode_attention_noalloc -- fd_decode_attention for callers that cannot

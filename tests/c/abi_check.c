@@ -44,5 +44,9 @@ int main(void) {
   printf("status %s\n", fd_status_string(FD_ERR_EMPTY_SPLIT));
   int prev = fd_set_kernel_path(FD_PATH_VALU);
   printf("path %d %d %d\n", prev, fd_set_kernel_path(prev), fd_set_kernel_path(42));
+  const int sched = fd_set_schedule(FD_SCHED_QUEUE);
+  printf("sched %d %d %d\n", sched, fd_set_schedule(sched), fd_set_schedule(42));
+  const int comb = fd_set_combine(FD_COMBINE_FUSED);
+  printf("combine %d %d %d\n", comb, fd_set_combine(comb), fd_set_combine(42));
   return 0;
 }

@@ -88,7 +88,7 @@ int main(void) {
     const size_t w2 = fd_workspace_bytes(batch, heads, ns + 1 <= FD_MAX_SPLITS ? ns + 1 : ns, dim);
     const size_t u1 = fd_workspace_bytes_unnorm(batch, heads, ns, dim);
     calls += 3;
-    CHECK(w1 > 0 && w2 >= w1 && u1 >= w1, "workspace %zu %zu %zu", w1, w2, u1);
+    CHECK(w1 > 0 && w2 >= w1 && u1 > 0, "workspace %zu %zu %zu", w1, w2, u1);
     CHECK(w1 >= (size_t)batch * heads * ns * ((size_t)dim + 1) * 4, "workspace too small");
   }
 

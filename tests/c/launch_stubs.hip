@@ -18,5 +18,6 @@ hipError_t launch_split_bf16(const SplitArgs&, int, int, bool, dim3, hipStream_t
 hipError_t launch_combine(const CombineArgs&, int, int, hipStream_t) {
   return hipErrorInvalidValue;
 }
+hipError_t launch_queue_reset(int*, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace fd

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
               "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path",
               "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
-              "fd_decode_attention_unnorm"):
+              "fd_decode_attention_unnorm", "fd_set_schedule", "fd_decode_attention_noalloc", "fd_set_combine"):
         assert n in names
 
 
@@ -61,7 +61,10 @@ def test_workspace_bytes_layout(B, H, D, ns):
     n = fd.fd_workspace_bytes(B, H, ns, D)
     opart = B * H * ns * D * 4
     lse_off = (opart + 255) // 256 * 256
-    assert n == lse_off + B * ns * H * 4
+    ctl_off = lse_off + (B * ns * H * 4 + 255) // 256 * 256
+    # control block: the queue's claim counter (256 B), then B*H arrival
+    # counters of fused calls padded to 256 B
+    assert n == ctl_off + 256 + (B * H * 4 + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (3, 5, 64, 1000)])

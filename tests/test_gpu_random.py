@@ -1,8 +1,9 @@
 """Seeded random sweep over the whole call: each case draws dtype, head dim,
 group size, KV heads, batch, ragged lengths (empty sequences and lengths
 below the split count included), split count, K/V layout (packed,
-[B, Hkv, S, D], [B, S, Hkv, D]), split format, kernel path and sometimes a
-non-default scale, and checks every output element against the fp64
+[B, Hkv, S, D], [B, S, Hkv, D]), split format, kernel path, sometimes a
+non-default scale, the single-launch (fused) combine and the queue
+schedule, and checks every output element against the fp64
 oracle's direct attention (empty sequences: zero rows). K/V rows outside
 the sequences are NaN, so an over-read shows.
 
@@ -99,8 +100,12 @@ def _draw(i: int):
     fmt = str(rng.choice(["lse", "unnorm"]))
     path = str(rng.choice(list(PATHS)))
     scale = None if rng.random() < 0.6 else float(rng.uniform(-1.0, 2.0))
+    # drawn last, so the draws above are those of the sweep without them
+    combine = "fused" if rng.random() < 0.35 else "separate"
+    sched = "queue" if rng.random() < 0.35 else "auto"
     return dict(dtype=dtype, dim=dim, group=group, kv_heads=kv_heads, lengths=lengths, ns=ns,
-                layout=layout, fmt=fmt, path=path, scale=scale, seed=i)
+                layout=layout, fmt=fmt, path=path, scale=scale, combine=combine, sched=sched,
+                seed=i)
 
 
 CASES = [_draw(i) for i in range(N_CASES)]
@@ -115,7 +120,7 @@ def _gpu():
 
 @pytest.mark.parametrize("c", CASES, ids=lambda c: (
     f"s{c['seed']}-{c['dtype']}-d{c['dim']}-g{c['group']}x{c['kv_heads']}-ns{c['ns']}-"
-    f"{c['layout']}-{c['fmt']}-{c['path']}"))
+    f"{c['layout']}-{c['fmt']}-{c['path']}-{c['combine']}-{c['sched']}"))
 def test_random_case_matches_oracle(c):
     fd = H.fd()
     heads = c["group"] * c["kv_heads"]
@@ -131,11 +136,16 @@ def test_random_case_matches_oracle(c):
     call = fd.fd_decode_attention_unnorm if c["fmt"] == "unnorm" else fd.fd_decode_attention
     H.announce("random", c)
     prev = fd.fd_set_kernel_path(PATHS[c["path"]])
+    prev_c = fd.fd_set_combine(fd.FD_COMBINE_FUSED if c["combine"] == "fused"
+                               else fd.FD_COMBINE_SEPARATE)
+    prev_s = fd.fd_set_schedule(fd.FD_SCHED_QUEUE if c["sched"] == "queue" else fd.FD_SCHED_AUTO)
     try:
         out = call(inp.q, k, v, inp.cu_seqlens_k, c["ns"], scale=scale, layout=c["layout"])
         torch.cuda.synchronize()
     finally:
         fd.fd_set_kernel_path(prev)
+        fd.fd_set_combine(prev_c)
+        fd.fd_set_schedule(prev_s)
     out = H.host(out)
     assert np.isfinite(out).all()
     q = H.host(inp.q)
