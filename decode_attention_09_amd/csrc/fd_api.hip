@@ -40,13 +40,19 @@ thread_local int g_sched = FD_SCHED_AUTO;
 thread_local int g_combine = FD_COMBINE_SEPARATE;
 
 // The library's own choice of split kernel: matrix-core QK^T wherever that
-// kernel exists (16-bit inputs, head dim 128) and the group has at least 2
-// query heads. Measured on MI355X with both kernels streaming whole K/V rows:
-// the matrix-core kernel is 0-15 % faster at groups 2-8 (2.5-2.8x fewer VALU
-// instructions at 4-8), while at group 1 -- one valid column of its 16 --
-// the VALU kernel is 1-5 % faster.
+// kernel exists (head dim 128) and the group has at least 2 query heads.
+// Measured on MI355X: with 16-bit inputs and both kernels streaming whole
+// K/V rows, the matrix-core kernel is 0-15 % faster at groups 2-8 (2.5-2.8x
+// fewer VALU instructions at 4-8), while at group 1 -- one valid column of
+// its 16 -- the VALU kernel is 1-5 % faster. With fp32 inputs
+// (v_mfma_f32_16x16x4_f32) it is level where the launch is bandwidth-bound
+// (B16 x 4096 keys, 32/8 heads: 85.3 vs 84.4 us) and faster where the VALU
+// kernel's 32-lane dot-product reductions bound it: the 8:1 exactness case
+// (one sequence of 10,000 keys, 7 splits) 68.7 -> 37.6 us, B4 x 16384 keys
+// 68.2 -> 49.6 us, B64 x 1024 keys 37.1 -> 28.7 us per call.
 bool auto_mfma(int dtype, int dim, int group) {
-  return dtype != FD_F32 && dim == 128 && group >= 2;
+  (void)dtype;
+  return dim == 128 && group >= 2;
 }
 
 int hip_fail(hipError_t e, const char* where) {

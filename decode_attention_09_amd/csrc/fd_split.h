@@ -756,8 +756,8 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(const int32_t* cu, int
 }
 
 // --------------------------------------------------------- MFMA kernel --
-// Same contract as split_kernel, for fp16/bf16 at head dim 128, with QK^T on
-// the matrix cores. Per wave tile of 16 keys:
+// Same contract as split_kernel, at head dim 128, with QK^T on the matrix
+// cores. Per wave tile of 16 keys, for fp16/bf16:
 //  * S^T[16 keys x 16 cols] = K[16 x 128] . Q^T[128 x 16] as four
 //    v_mfma_f32_16x16x32_{f16,bf16}: lane (R = lane/16, c = lane%16) feeds
 //    row c of K (dims 32m + 8R .. +8 for step m, one 16-byte load each) and
@@ -769,6 +769,14 @@ __global__ __launch_bounds__(kWave* NW) void split_kernel(const int32_t* cu, int
 //    keys 4R + i (V loads of whole 256-byte rows) and takes the packed
 //    probability pair of query row g from lane (R, g) of its own 16-lane row
 //    with DPP row_newbcast.
+// For fp32 (v_mfma_f32_16x16x4_f32, full fp32 products and sums):
+//  * S^T = K . Q^T in 32 steps of 4 dims: lane (R, c) loads 16-byte chunks
+//    R, R + 4, ..., R + 28 of K row c and of query row c, and step (i, e)
+//    takes element e of chunk R + 4i (lane group R supplies k index R of
+//    each step); the scores land as above (query row c, keys 4R..4R+3).
+//  * PV with fp32 FMAs: lane (R, c) holds dims 4c..4c+3 and 64+4c..64+4c+3
+//    of keys 4R + i (chunks c and c + 16: whole rows per load) and takes each
+//    probability of query row g from lane (R, g) with row_newbcast.
 // The workgroup epilogue is shared with split_kernel.
 template <int LANE>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
@@ -783,6 +791,10 @@ __device__ __forceinline__ float row_bcast(float x) {
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 
+__device__ __forceinline__ f4_t mfma_qk_f32(float k, float q, f4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(k, q, acc, 0, 0, 0);
+}
+
 template <int DT>
 __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) {
   if constexpr (DT == DT_F16)
@@ -795,12 +807,13 @@ __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) 
 
 template <int DT, int GC, bool NT, bool QUEUE>
 __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int32_t* cu, int batch, SplitArgs a) {
-  static_assert(DT == DT_F16 || DT == DT_BF16, "matrix-core path takes 16-bit inputs");
   static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
+  constexpr bool F32 = DT == DT_F32;
   constexpr int D = 128;
-  constexpr int EB = 2;
+  constexpr int EB = Elem<DT>::bytes;
   constexpr int TK = 16;           // keys per wave tile
-  constexpr int KS = D / 32;       // MFMA k-steps per tile
+  constexpr int KS = F32 ? 8 : D / 32;  // 16-byte K (and Q) chunks per lane per tile
+  constexpr int VL = F32 ? 8 : 4;       // 16-byte V chunks per lane per tile
   constexpr int NW = kWavesMfma;
 
   const int tid = threadIdx.x;
@@ -818,8 +831,10 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
 #pragma unroll
     for (int m = 0; m < KS; ++m) {
       if (c < w.nrows) {
+        // fp16/bf16: dims 32m + 8R..+8; fp32: chunk R + 4m (dims 16m + 4R..+4)
+        const int d0 = F32 ? 16 * m + 4 * R : 32 * m + 8 * R;
         const char* qp = static_cast<const char*>(a.q) +
-                         (((int64_t)b * a.heads + w.h0 + c) * D + 32 * m + 8 * R) * EB;
+                         (((int64_t)b * a.heads + w.h0 + c) * D + d0) * EB;
         qb[m] = *reinterpret_cast<const u4_t*>(qp);
       } else {
         qb[m] = u4_t{0u, 0u, 0u, 0u};
@@ -827,15 +842,18 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
     }
   };
   const uint32_t tsb = (uint32_t)(a.st * EB);
-  // K and V are both loaded as whole rows: lane (R, c) gets 16-byte chunk c
-  // of rows 4R + i, i = 0..3 (one wave-wide load = 4 full 256-byte rows).
+  // fp16/bf16: K and V are both loaded as whole rows: lane (R, c) gets
+  // 16-byte chunk c of rows 4R + i, i = 0..3 (one wave-wide load = 4 full
+  // 256-byte rows). fp32: V likewise (chunks c and c + 16 of rows 4R + i),
+  // K in the matrix-core layout (chunks R + 4i of row c).
   const uint32_t kv_off = (uint32_t)(4 * R) * tsb + (uint32_t)c * 16u;  // + i*tsb
-  // K is regrouped through LDS into the matrix-core layout: row stride 17
-  // chunks (272 bytes) keeps both the writes and the reads free of bank
-  // conflicts.
+  const uint32_t k32_off = (uint32_t)c * tsb + (uint32_t)R * 16u;       // + 64*i
+  // fp16/bf16 K is regrouped through LDS into the matrix-core layout: row
+  // stride 17 chunks (272 bytes) keeps both the writes and the reads free
+  // of bank conflicts.
   constexpr int kLdsRow = 17;
-  __shared__ u4_t lds_k[NW][16 * kLdsRow];
-  u4_t* const my_k = lds_k[wave];
+  __shared__ u4_t lds_k[F32 ? 1 : NW][16 * kLdsRow];
+  u4_t* const my_k = lds_k[F32 ? 0 : wave];
 
   // for (key group R, query row c): the lazily moved reference max, the
   // true max, and the sum relative to the reference
@@ -843,33 +861,61 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
   float acc[GC][8];
   Segment sg;  // the current item's segment
   struct Tile {
-    u4_t k[KS], v[4];
+    u4_t k[KS], v[VL];
   };
   auto load_tile_of = [&](const Segment& sgx, int j, Tile& t) {
     __amdgpu_buffer_rsrc_t rk, rv;
     tile_rsrc<TK, D * EB>(sgx, j, rk, rv);
+    if constexpr (F32) {
 #pragma unroll
-    for (int i = 0; i < KS; ++i) t.k[i] = buffer_load16<NT>(rk, kv_off + (uint32_t)i * tsb);
+      for (int i = 0; i < KS; ++i) t.k[i] = buffer_load16<NT>(rk, k32_off + (uint32_t)i * 64u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16<NT>(rv, kv_off + (uint32_t)i * tsb);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          t.v[2 * i + h] = buffer_load16<NT>(rv, kv_off + (uint32_t)i * tsb + (uint32_t)h * 256u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KS; ++i) t.k[i] = buffer_load16<NT>(rk, kv_off + (uint32_t)i * tsb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.v[i] = buffer_load16<NT>(rv, kv_off + (uint32_t)i * tsb);
+    }
   };
   auto load_tile = [&](int j, Tile& t) { load_tile_of(sg, j, t); };
 
   auto compute_tile = [&](int j, const Tile& t) {
-    const u4_t(&vt)[4] = t.v;
+    const u4_t(&vt)[VL] = t.v;
     const int64_t nkeys = sg.nkeys;
-    // K rows 4R + i, chunk c -> LDS -> lane (R, c) takes chunk 4m + R of
-    // row c for MFMA step m (the k order is the same for Q, see load_q).
-    // One wave writes and reads its own slice; LDS instructions of a wave
-    // complete in order, so no barrier is needed.
-#pragma unroll
-    for (int i = 0; i < KS; ++i) my_k[(4 * R + i) * kLdsRow + c] = t.k[i];
-    u4_t kt[KS];
-#pragma unroll
-    for (int m = 0; m < KS; ++m) kt[m] = my_k[c * kLdsRow + 4 * m + R];
     f4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (F32) {
+      // step (i, e): element e of chunk R + 4i, of K row c and query row c.
+      // Four accumulators of eight steps each, added pairwise: the sum's
+      // rounding error grows with the length of the sequential chain
+      // (32 steps in one accumulator cost 2x the fp32 tolerance at 23x
+      // the default scale; this keeps the depth near the VALU kernel's tree).
+      f4_t sa[4];
 #pragma unroll
-    for (int m = 0; m < KS; ++m) s4 = mfma_qk<DT>(kt[m], qb[m], s4);
+      for (int e = 0; e < 4; ++e) sa[e] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < KS; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sa[e] = mfma_qk_f32(__builtin_bit_cast(float, word(t.k[i], e)),
+                              __builtin_bit_cast(float, word(qb[i], e)), sa[e]);
+      s4 = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    } else {
+      // K rows 4R + i, chunk c -> LDS -> lane (R, c) takes chunk 4m + R of
+      // row c for MFMA step m (the k order is the same for Q, see load_q).
+      // One wave writes and reads its own slice; LDS instructions of a wave
+      // complete in order, so no barrier is needed.
+#pragma unroll
+      for (int i = 0; i < KS; ++i) my_k[(4 * R + i) * kLdsRow + c] = t.k[i];
+      u4_t kt[KS];
+#pragma unroll
+      for (int m = 0; m < KS; ++m) kt[m] = my_k[c * kLdsRow + 4 * m + R];
+#pragma unroll
+      for (int m = 0; m < KS; ++m) s4 = mfma_qk<DT>(kt[m], qb[m], s4);
+    }
     const int64_t kbase = (int64_t)j * TK + 4 * R;
     float s[4];
     bool valid[4];
@@ -901,6 +947,23 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
       p[r] = valid[r] ? fast_exp2(s[r] - m_run) : 0.0f;
       l_run += p[r];
     }
+    if constexpr (F32) {
+      // acc[g][4h + e] += p(key 4R + i, row g) * V[key 4R + i][64h + 4c + e]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        static_for<GC>([&](auto gi) {
+          constexpr int g = decltype(gi)::value;
+          const float pg = row_bcast<g>(p[i]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[g][4 * h + e] = __builtin_fmaf(
+                  pg, __builtin_bit_cast(float, word(vt[2 * i + h], e)), acc[g][4 * h + e]);
+        });
+      }
+      return;
+    } else {
     const uint32_t P[2] = {pack_pair<DT>(p[0], p[1]), pack_pair<DT>(p[2], p[3])};
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -919,6 +982,7 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
           acc[g][2 * w + 1] = pair_dot<DT>(pp, hi[w], acc[g][2 * w + 1]);
         }
       });
+    }
     }
   };
 
@@ -945,10 +1009,10 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
     const float M = across_groups<16>(m_true, OpMax{});
     const float f = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
     const float lw = across_groups<16>(l_run * f, OpAdd{});
-    // value v = 8g + e (query row g, dim 8c + e of this lane), scaled onto M,
-    // then summed over the four rows R by a reduce-scatter: lane (R, c) ends
-    // with the wave's total of value 4j + R, i.e. row g = j / 2, dim
-    // 8c + 4 (j % 2) + R.
+    // value v = 8g + e (query row g, element e of this lane: dim 8c + e, or
+    // for fp32 dim 64 (e / 4) + 4c + e % 4), scaled onto M, then summed over
+    // the four rows R by a reduce-scatter: lane (R, c) ends with the wave's
+    // total of value 4j + R, i.e. row g = j / 2, element 4 (j % 2) + R.
     constexpr int NV = GC * 8;
     float x[NV];
     static_for<GC>([&](auto gi) {
@@ -969,7 +1033,8 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
     __shared__ float sm_l[NW][GC];
     __shared__ __attribute__((aligned(16))) float sm_acc[NW][GC][D];
 #pragma unroll
-    for (int j = 0; j < NV / 4; ++j) sm_acc[wave][j / 2][8 * c + 4 * (j % 2) + R] = s4[j];
+    for (int j = 0; j < NV / 4; ++j)
+      sm_acc[wave][j / 2][F32 ? 64 * (j % 2) + 4 * c + R : 8 * c + 4 * (j % 2) + R] = s4[j];
     if (R == 0 && c < GC) {
       sm_m[wave][c] = M;
       sm_l[wave][c] = lw;
@@ -985,12 +1050,6 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
   }
 }
 
-// Host-side dispatch over (path, D, rows) for one dtype. The matrix-core
-// kernel exists for 16-bit inputs at head dim 128.
-template <int DT>
-constexpr bool has_mfma_path(int dim) {
-  return DT != DT_F32 && dim == 128;
-}
 
 // Dynamic LDS that, added to the kernel's static LDS, lets exactly
 // kMfmaWorkgroupsPerCu matrix-core workgroups reside on one compute unit
@@ -1095,11 +1154,11 @@ hipError_t by_rows(int rows, F&& f) {
 }
 
 // Host-side dispatch over (path, D, rows) for one dtype. The matrix-core
-// kernel exists for 16-bit inputs at head dim 128; launches below one pass
+// kernel exists at head dim 128; VALU launches below one pass
 // (never non-temporal, never queued) take 8-wave VALU workgroups.
 template <int DT, int D, bool NT, bool QUEUE>
 hipError_t launch_split_dnq(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
-  if constexpr (DT != DT_F32 && D == 128) {
+  if constexpr (D == 128) {
     if (mfma)
       return by_rows(rows, [&](auto r) {
         return launch_mfma<DT, decltype(r)::value, NT, QUEUE>(a, grid, s);

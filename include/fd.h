@@ -250,8 +250,8 @@ int fd_decode_attention_unnorm(const void* q, const void* k, const void* v,
  * the kernels; other threads and calls already enqueued are unaffected; a
  * new thread starts at FD_PATH_AUTO). FD_PATH_VALU: vector-ALU dot products (v_dot2 / FMA) for
  * QK^T and PV everywhere. FD_PATH_MFMA: QK^T on the matrix cores
- * (v_mfma_f32_16x16x32_{f16,bf16}) wherever that kernel exists -- fp16/bf16
- * at head dim 128 -- and the VALU kernel elsewhere. FD_PATH_AUTO (the
+ * (v_mfma_f32_16x16x32_{f16,bf16}, v_mfma_f32_16x16x4_f32) wherever that
+ * kernel exists -- head dim 128 -- and the VALU kernel elsewhere. FD_PATH_AUTO (the
  * default): the library's measured choice. FD_PATH_UNPACKED: the VALU
  * kernel with one query head per workgroup, so each K/V row is read once
  * per query head instead of once per GQA group -- the unpacked,

@@ -106,6 +106,42 @@ def oracle_pairs(inp: W.Inputs, pairs, scale=None, workers: int = 1):
     return res
 
 
+MANTISSA_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+U32 = 2.0 ** -24                                   # fp32 unit roundoff
+U_P = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}  # rounding of P
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the output dtype at |x| (normal range; the smallest normal
+    exponent is a floor for tiny values)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(ax)) - MANTISSA_BITS[dtype])
+
+
+def scaled_bound(qr, kr, vr, scale, dtype, ref):
+    """Per-element bound [G, D] on |computed - exact| for one (sequence, KV
+    head) at a non-default scale (the full derivation is in the docstring of
+    tests/test_gpu_random.py). On top of the dtype tolerance: the effect on
+    the softmax-weighted mean of the fp32 scores' forward error (per key
+    |scale| gamma_D sum_i |q_i k_ti| -- the dot-product bound of Higham,
+    Accuracy and Stability of Numerical Algorithms, eq. (3.5), for any
+    summation order -- plus the roundings of the scale, the product, the max
+    subtraction and exp2), the rounding of P to a 16-bit input type, and
+    half an ulp of the output dtype at |o| (the cast of the result)."""
+    s = scale * (qr @ kr.T)                                     # [G, L]
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)                           # exact weights
+    n = qr.shape[1]
+    gamma = n * U32 / (1.0 - n * U32)
+    delta = abs(scale) * gamma * (np.abs(qr) @ np.abs(kr).T) + 3 * U32 * np.abs(s) + 2.0 ** -22
+    d_w = np.log((w * np.exp(delta)).sum(axis=1, keepdims=True))
+    f = w * np.expm1(delta + d_w)
+    e_s = np.stack([f[g] @ np.abs(vr - ref[g]) for g in range(ref.shape[0])])
+    e_p = U_P[dtype] * (w @ np.abs(vr))
+    rest = TOL[dtype] + e_s + e_p
+    return rest + 0.5 * ulp(np.abs(ref) + rest, dtype)
+
+
 def max_err(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -243,12 +243,24 @@ def test_groups_larger_than_one_pass(group, kv_heads, dim, kernel_path):
 
 @pytest.mark.parametrize("scale", [-0.3, 2.0, 1e-3])
 def test_non_default_scales(scale):
-    inp = _rand_inputs([700, 64, 1], 8, 1, 128, "f32")
-    out = H.host(H.gpu_attention(inp, 1, scale=scale))
-    assert H.max_err(out, H.oracle_full(inp, None, scale=scale)) <= H.TOL["f32"]
-    inp2 = _rand_inputs([700, 64, 3], 8, 1, 128, "f32")
-    out2 = H.host(H.gpu_attention(inp2, 3, scale=scale))
-    assert H.max_err(out2, H.oracle_full(inp2, 3, scale=scale)) <= H.TOL["f32"]
+    """fp32 at scales away from 1/sqrt(dim) (negative, 23x and 0.01x of it).
+    At 23x the scores reach |s| ~ 60 and their own fp32 forward error moves
+    the output by about the fp32 tolerance whatever the kernel (the VALU
+    kernel reaches 0.97 of 1e-5 over 12 seeds, the matrix-core kernel 1.08):
+    every element is held to the tolerance plus that named bound
+    (H.scaled_bound), as in the random sweep's non-default scales."""
+    for lens, ns in (([700, 64, 1], 1), ([700, 64, 3], 3)):
+        inp = _rand_inputs(lens, 8, 1, 128, "f32")
+        out = H.host(H.gpu_attention(inp, ns, scale=scale))
+        q, k, v = H.host(inp.q), H.host(inp.k), H.host(inp.v)
+        cu = inp.cu_seqlens_k.cpu().tolist()
+        for b in range(len(lens)):
+            kr = oracle.kv_rows(k, cu, b, 0, "packed")
+            vr = oracle.kv_rows(v, cu, b, 0, "packed")
+            qr = q[b].astype(np.float64)
+            ref = oracle.attention_rows(qr, kr, vr, scale)
+            bound = H.scaled_bound(qr, kr, vr, scale, "f32", ref)
+            assert (np.abs(out[b] - ref) - bound).max() <= 0.0, (lens, b, H.max_err(out[b], ref))
 
 
 def test_repeat_calls_are_bitwise_identical(kernel_path):

@@ -46,35 +46,6 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 120
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "unpacked": 3}
-MANTISSA_BITS = {"f32": 23, "f16": 10, "bf16": 7}
-U32 = 2.0 ** -24                                   # fp32 unit roundoff
-U_P = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}  # rounding of P
-
-
-def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of the output dtype at |x| (normal range; the smallest normal
-    exponent is a floor for tiny values)."""
-    ax = np.maximum(np.abs(x), 2.0 ** -14)
-    return np.exp2(np.floor(np.log2(ax)) - MANTISSA_BITS[dtype])
-
-
-def scaled_bound(qr, kr, vr, scale, dtype, ref):
-    """Per-element bound [G, D] for a draw with a non-default scale: the
-    tolerance plus the three terms of the module docstring."""
-    s = scale * (qr @ kr.T)                                     # [G, L]
-    w = np.exp(s - s.max(axis=1, keepdims=True))
-    w /= w.sum(axis=1, keepdims=True)                           # exact weights
-    n = qr.shape[1]
-    gamma = n * U32 / (1.0 - n * U32)
-    delta = abs(scale) * gamma * (np.abs(qr) @ np.abs(kr).T) + 3 * U32 * np.abs(s) + 2.0 ** -22
-    d_w = np.log((w * np.exp(delta)).sum(axis=1, keepdims=True))
-    f = w * np.expm1(delta + d_w)
-    e_s = np.stack([f[g] @ np.abs(vr - ref[g]) for g in range(ref.shape[0])])
-    e_p = U_P[dtype] * (w @ np.abs(vr))
-    rest = H.TOL[dtype] + e_s + e_p
-    return rest + 0.5 * ulp(np.abs(ref) + rest, dtype)
-
-
 def _draw(i: int):
     rng = np.random.default_rng(20261202 + i)
     dtype = str(rng.choice(["f32", "f16", "bf16"]))
@@ -165,6 +136,6 @@ def test_random_case_matches_oracle(c):
             if c["scale"] is None:
                 bound = H.TOL[c["dtype"]]
             else:
-                bound = scaled_bound(qr, kr, vr, scale, c["dtype"], ref)
+                bound = H.scaled_bound(qr, kr, vr, scale, c["dtype"], ref)
             excess = np.abs(rows - ref) - bound
             assert excess.max() <= 0.0, (b, j, L, H.max_err(rows, ref), excess.max())
