@@ -298,6 +298,82 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     return res
 
 
+# The split-count sweeps the planner's time model is fitted to: the three
+# settings of 04_flash_decoding.py demo 4 (16/2 heads) and four Llama-8B
+# shapes, whole calls replayed from a HIP graph (no host issue cost).
+FIT_SWEEPS = [
+    ("fd_ubench_b1_l65536_h16kv2_d128_f16", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128]),
+    ("fd_ubench_b8_l8192_h16kv2_d128_f16", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128]),
+    ("fd_ubench_b64_l2048_h16kv2_d128_f16", [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128]),
+    ("llama8b_b1_l65536_h32kv8_d128_bf16_ns1", [1, 2, 4, 8, 16, 32, 64, 128]),
+    ("llama8b_b16_l8192_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
+    ("llama8b_b1_l8192_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
+    ("llama8b_b16_l1024_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
+]
+
+
+def model_call_us(p, units, ns, cus, key_bytes, max_len, partial_bytes):
+    """The planner's time model for uniform lengths (fd_api.hip, model_call_us),
+    with parameters p = (launch, workgroup, rate, contention, combine,
+    combine per MB) in us and bytes/us."""
+    launch, wg_us, rate, contention, comb, comb_mb = p
+    wg_bytes = math.ceil(max_len / ns) * key_bytes
+    t, rem = launch, units * ns
+    while rem > 0:
+        n = min(rem, cus)
+        t += wg_us + wg_bytes * (1.0 / rate + n / contention)
+        rem -= n
+    if ns > 1:
+        t += comb + comb_mb * partial_bytes * 1e-6
+    return t
+
+
+def fit_planner(steps: int, warmup: int):
+    """Measure FIT_SWEEPS, fit the time model's six constants (least squares
+    on relative error), and print one JSON line: the fitted constants, the
+    fit's error, and per point the measured time, the library's modelled
+    time (fd_plan_time_us, its compiled-in constants) and the refit's."""
+    import torch
+    from scipy.optimize import least_squares
+    import decode_attention_09_amd as fd
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pts = []
+    for name, splits in FIT_SWEEPS:
+        w = workload_by_name(name)
+        for ns in splits:
+            r = run(w, steps, warmup, 0.0, ns_override=ns, graph=True)
+            G = w.group
+            pts.append(dict(workload=name, ns=ns, batch=w.batch, heads=w.heads,
+                            kv_heads=w.kv_heads, dim=w.dim, kv_len=w.kv_len,
+                            units=w.batch * w.kv_heads * math.ceil(G / 8),
+                            key_bytes=2 * w.dim * w.elem_bytes,
+                            partial_bytes=w.batch * w.heads * ns * (w.dim + 1) * 4,
+                            measured_us=r["us_per_call"]))
+            print(f"[fit] {name} ns={ns} {r['us_per_call']:.2f} us", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+
+    def resid(p):
+        return [model_call_us(p, x["units"], x["ns"], cus, x["key_bytes"], x["kv_len"],
+                              x["partial_bytes"]) / x["measured_us"] - 1.0 for x in pts]
+    fit = least_squares(resid, [3.0, 1.0, 5e4, 1.5e7, 2.5, 0.7],
+                        bounds=([0, 0, 1e3, 1e5, 0, 0], [50, 50, 1e7, 1e9, 50, 100]))
+    code = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}
+    for x in pts:
+        w = workload_by_name(x["workload"])
+        x["library_model_us"] = round(fd.fd_plan_time_us(
+            w.batch, w.heads, w.kv_heads, w.dim, code[w.dtype], [w.kv_len] * w.batch, x["ns"],
+            num_cus=cus), 2)
+        x["refit_model_us"] = round(model_call_us(fit.x, x["units"], x["ns"], cus,
+                                                  x["key_bytes"], x["kv_len"],
+                                                  x["partial_bytes"]), 2)
+    rel = [abs(v) for v in fit.fun]
+    names = ["launch_us", "workgroup_us", "rate_bytes_per_us", "contention_bytes_per_us",
+             "combine_us", "combine_us_per_mb"]
+    print(json.dumps({"fit": dict(zip(names, [round(v, 4) for v in fit.x])),
+                      "rms_rel": round(math.sqrt(sum(v * v for v in rel) / len(rel)), 4),
+                      "max_rel": round(max(rel), 4), "cus": cus, "points": pts}), flush=True)
+
+
 def copy_calibration(mib: int):
     """Ten device-to-device copies of a mib-MiB buffer: a kernel that reads
     and writes exactly mib MiB per launch, to scale the HBM byte counters."""
@@ -344,12 +420,17 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time the calls as one captured HIP graph replay instead of eager "
                          "calls (takes the host's per-call issue cost out; for small shapes)")
+    ap.add_argument("--fit-planner", action="store_true",
+                    help="measure the split-count sweeps and fit the planner's time model")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 10 times (reference for the "
                          "FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.fit_planner:
+        fit_planner(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -21,6 +21,7 @@ __all__ = [
     "fd_decode_attention_unnorm", "workspace_views_unnorm", "fd_decode_attention_noalloc",
     "FD_NOALLOC_SCRATCH_BYTES", "fd_set_schedule", "FD_SCHED_AUTO", "FD_SCHED_STATIC",
     "FD_SCHED_QUEUE", "fd_set_combine", "FD_COMBINE_SEPARATE", "FD_COMBINE_FUSED",
+    "fd_plan_time_us",
 ]
 
 FD_F32, FD_F16, FD_BF16 = 0, 1, 2
@@ -74,6 +75,9 @@ def load_library():
     lib.fd_plan_splits.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), i32,
                                    i32, ctypes.POINTER(ctypes.c_int)]
     lib.fd_plan_splits.restype = i32
+    lib.fd_plan_time_us.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), i32,
+                                    i32]
+    lib.fd_plan_time_us.restype = ctypes.c_double
     lib.fd_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.fd_workspace_bytes.restype = ctypes.c_size_t
     lib.fd_decode_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp,
@@ -215,6 +219,18 @@ def fd_plan_splits(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, 
     _check(lib.fd_plan_splits(batch, heads, kv_heads, dim, dtype, arr, num_cus, max_splits,
                               ctypes.byref(out)), "fd_plan_splits")
     return out.value
+
+
+def fd_plan_time_us(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, seqlens,
+                    num_splits: int, num_cus: int = 0) -> float:
+    """The planner's modelled time (us) of one call with num_splits splits."""
+    lens = [int(x) for x in seqlens]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    t = load_library().fd_plan_time_us(batch, heads, kv_heads, dim, dtype, arr, num_cus,
+                                       int(num_splits))
+    if t < 0:
+        raise ValueError("fd_plan_time_us: bad arguments")
+    return float(t)
 
 
 def fd_workspace_bytes(batch: int, heads: int, num_splits: int, dim: int) -> int:

@@ -66,10 +66,23 @@ constexpr int64_t kMaxWorkgroups = int64_t(1) << 24;
 // Fewest keys per split the planner will create (flash_decode_splitk.py's
 // default of one split per 256 keys).
 constexpr int kPlanMinKeysPerSplit = 256;
-// Fixed cost of one split workgroup (launch, first-tile latency, epilogue),
-// as the equivalent bytes a compute unit streams in that time (measured on
-// MI355X: about 1 us at ~25-30 GB/s per CU).
-constexpr double kPlanWorkgroupBytes = 32.0 * 1024.0;
+// Time model of one call (split launch + combine launch), fitted on MI355X
+// to 74 measured calls -- the split-count sweeps of 04_flash_decoding.py
+// demo 4 (16/2 heads at B1 x 64K, B8 x 8K, B64 x 2K, 14 split counts each)
+// and four Llama-8B-shaped sweeps -- with relative RMS error 4.7 % (largest
+// 15 %); `python bench.py --fit-planner` re-measures and refits. A launch of
+// w workgroups runs rounds of min(CUs, remaining) workgroups; a round costs
+// a fixed workgroup time plus its bytes at a per-byte time that grows with
+// the number of workgroups streaming at once (one workgroup alone streams
+// ~51 GB/s; 256 together ~27 GB/s each):
+//   T_split = launch + sum over rounds (workgroup + bytes * (1/rate + n/contention))
+//   T_call  = T_split + [ns > 1] (combine + combine_per_mb * partial MB)
+constexpr double kModelLaunchUs = 3.848;
+constexpr double kModelWorkgroupUs = 0.972;
+constexpr double kModelRateBytesPerUs = 50960.0;          // one workgroup alone
+constexpr double kModelContentionBytesPerUs = 14.825e6;   // n/this: per-byte time of n at once
+constexpr double kModelCombineUs = 2.537;
+constexpr double kModelCombineUsPerMB = 0.7034;           // per MB of fp32 partials
 
 // Compute units of the current device, cached per device ordinal.
 constexpr int kMaxDevices = 64;
@@ -403,6 +416,69 @@ int attention_impl(Format fmt, const void* q, const void* k, const void* v,
   return combine_impl(fmt, workspace, batch, heads, dim, num_splits, out, stream, dtype);
 }
 
+// Modelled time (us) of a call with ns splits (see the model above). With
+// unequal lengths, workgroups are handed out as compute units free up, which
+// finishes within the average load plus the largest workgroup
+// (list-scheduling bound), at the rate of min(CUs, workgroups) at once.
+double model_call_us(int64_t units, int64_t ns, int cus, double key_bytes, int64_t max_len,
+                     double all_bytes, bool uniform, double partial_bytes) {
+  const int64_t wgs = units * ns;
+  const double wg_bytes = std::ceil((double)max_len / (double)ns) * key_bytes;
+  auto per_byte = [](double n) {
+    return 1.0 / kModelRateBytesPerUs + n / kModelContentionBytesPerUs;
+  };
+  double t = kModelLaunchUs;
+  if (uniform) {
+    for (int64_t rem = wgs; rem > 0;) {
+      const int64_t n = rem < cus ? rem : cus;
+      t += kModelWorkgroupUs + wg_bytes * per_byte((double)n);
+      rem -= n;
+    }
+  } else {
+    const double n = (double)(wgs < cus ? wgs : cus);
+    const double rounds = std::ceil((double)wgs / (double)cus);
+    t += rounds * kModelWorkgroupUs + (all_bytes / n + wg_bytes) * per_byte(n);
+  }
+  if (ns > 1) t += kModelCombineUs + kModelCombineUsPerMB * partial_bytes * 1e-6;
+  return t;
+}
+
+struct PlanInputs {
+  Sizes sz;
+  int64_t min_len, max_len, units;
+  double key_bytes, all_bytes, partial_bytes_per_split;
+  int cus;
+};
+
+int plan_inputs(int batch, int heads, int kv_heads, int dim, int dtype,
+                const int32_t* seqlens_host, int num_cus, PlanInputs* p) {
+  if (seqlens_host == nullptr) return FD_ERR_INVALID_ARG;
+  int st = check_common(batch, heads, kv_heads, dim, 1, dtype, &p->sz);
+  if (st != FD_OK) return st;
+  int64_t min_len = INT64_MAX, max_len = 0;
+  double total_keys = 0.0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t x = seqlens_host[b];
+    if (x < min_len) min_len = x;
+    if (x > max_len) max_len = x;
+    total_keys += (double)x;
+  }
+  if (min_len < 1) return FD_ERR_EMPTY_SPLIT;
+  if (num_cus < 0) return FD_ERR_INVALID_ARG;
+  if (num_cus == 0) {
+    st = device_cus(&num_cus);
+    if (st != FD_OK) return st;
+  }
+  p->min_len = min_len;
+  p->max_len = max_len;
+  p->units = (int64_t)batch * kv_heads * p->sz.row_chunks;
+  p->key_bytes = 2.0 * dim * (dtype == FD_F32 ? 4 : 2);  // one K + one V row
+  p->all_bytes = total_keys * (double)kv_heads * p->sz.row_chunks * p->key_bytes;
+  p->partial_bytes_per_split = (double)batch * heads * (dim + 1) * 4.0;
+  p->cus = num_cus;
+  return FD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,56 +502,27 @@ size_t fd_workspace_bytes_unnorm(int batch, int heads, int num_splits, int dim) 
 int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
                    const int32_t* seqlens_host, int num_cus, int max_splits,
                    int* num_splits_out) {
-  if (num_splits_out == nullptr || seqlens_host == nullptr) return FD_ERR_INVALID_ARG;
-  Sizes sz;
-  int st = check_common(batch, heads, kv_heads, dim, 1, dtype, &sz);
+  if (num_splits_out == nullptr) return FD_ERR_INVALID_ARG;
+  PlanInputs p;
+  const int st = plan_inputs(batch, heads, kv_heads, dim, dtype, seqlens_host, num_cus, &p);
   if (st != FD_OK) return st;
-  int64_t min_len = INT64_MAX, max_len = 0;
-  double total_keys = 0.0;
-  for (int b = 0; b < batch; ++b) {
-    const int64_t x = seqlens_host[b];
-    if (x < min_len) min_len = x;
-    if (x > max_len) max_len = x;
-    total_keys += (double)x;
-  }
-  if (min_len < 1) return FD_ERR_EMPTY_SPLIT;
-  if (num_cus < 0) return FD_ERR_INVALID_ARG;
-  if (num_cus == 0) {
-    const int st2 = device_cus(&num_cus);
-    if (st2 != FD_OK) return st2;
-  }
   if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
   // candidates: every split non-empty, the longest sequence keeps
   // >= kPlanMinKeysPerSplit keys per split, workgroup count bounded
-  int64_t cap = (max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
-  if (cap > min_len) cap = min_len;
+  int64_t cap = (p.max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
+  if (cap > p.min_len) cap = p.min_len;
   if (cap > max_splits) cap = max_splits;
-  const int64_t units = (int64_t)batch * kv_heads * sz.row_chunks;
-  while (cap > 1 && units * cap > kMaxWorkgroups) --cap;
+  while (cap > 1 && p.units * cap > kMaxWorkgroups) --cap;
   if (cap < 1) cap = 1;
-  // Estimated time, in bytes one compute unit streams, of a launch with ns
-  // splits on P = num_cus units: each unit runs `passes` rounds of
-  // workgroups (the workgroup count quantised to the CU count, the wave
-  // quantisation of 04_flash_decoding.py demo 4), each round paying the
-  // fixed workgroup cost. Equal lengths: every workgroup streams the same
-  // bytes, so a unit streams passes x that. Unequal lengths: workgroups are
-  // handed out as units free up, which finishes within the average load
-  // plus the largest workgroup (list-scheduling bound).
-  const double P = (double)num_cus;
-  const double key_bytes = 2.0 * dim * (dtype == FD_F32 ? 4 : 2);  // one K + one V row
-  const double all_bytes = total_keys * (double)kv_heads * sz.row_chunks * key_bytes;
-  const bool uniform = min_len == max_len;
+  // the least modelled time; ties to fewer splits. Launches of fewer
+  // workgroups than compute units are priced by the same rounds (one round),
+  // which is the wave quantisation of 04_flash_decoding.py demo 4 against
+  // the device's compute units.
   double best = 0.0;
   int choice = 1;
   for (int64_t ns = 1; ns <= cap; ++ns) {
-    const double wgs = (double)(units * ns);
-    const double passes = std::ceil(wgs / P);
-    const double wg_max = std::ceil((double)max_len / (double)ns) * key_bytes;
-    double t = passes * kPlanWorkgroupBytes;
-    if (uniform)
-      t += passes * wg_max;
-    else
-      t += all_bytes / P + wg_max;
+    const double t = model_call_us(p.units, ns, p.cus, p.key_bytes, p.max_len, p.all_bytes,
+                                   p.min_len == p.max_len, p.partial_bytes_per_split * ns);
     if (ns == 1 || t < best) {
       best = t;
       choice = (int)ns;
@@ -483,6 +530,16 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
   }
   *num_splits_out = choice;
   return FD_OK;
+}
+
+double fd_plan_time_us(int batch, int heads, int kv_heads, int dim, int dtype,
+                       const int32_t* seqlens_host, int num_cus, int num_splits) {
+  PlanInputs p;
+  if (num_splits < 1 || num_splits > FD_MAX_SPLITS) return -1.0;
+  if (plan_inputs(batch, heads, kv_heads, dim, dtype, seqlens_host, num_cus, &p) != FD_OK)
+    return -1.0;
+  return model_call_us(p.units, num_splits, p.cus, p.key_bytes, p.max_len, p.all_bytes,
+                       p.min_len == p.max_len, p.partial_bytes_per_split * num_splits);
 }
 
 int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_k,

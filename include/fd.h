@@ -115,17 +115,30 @@ typedef struct fd_kv_layout {
  * Rule (04_flash_decoding.py, demo 4; flash_decode_splitk.py's floor of
  * 256 keys per split; decode_attention_splitkv.py's non-empty rule): among
  * split counts that leave every split >= 1 key and the longest sequence
- * >= 256 keys per split, take the one with the least estimated time, where
- * the workgroup count is quantised to the compute-unit count (wave
- * quantisation: every CU runs ceil(workgroups / CUs) rounds, each paying a
- * fixed per-workgroup cost) and, for unequal lengths, the tail is bounded by
- * the largest split. Ties go to fewer splits.
+ * >= 256 keys per split, take the one with the least modelled call time
+ * (fd_plan_time_us). Ties go to fewer splits.
  * Returns FD_ERR_EMPTY_SPLIT if some length is < 1, FD_ERR_INVALID_ARG for
  * bad sizes, FD_ERR_HIP if the device query fails.
  */
 int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
                    const int32_t* seqlens_host, int num_cus, int max_splits,
                    int* num_splits_out);
+
+/*
+ * fd_plan_time_us -- the planner's modelled time, in microseconds, of one
+ * fd_decode_attention call (split launch plus, for num_splits > 1, the
+ * combine launch) with this split count: the time column of the split-count
+ * table of 04_flash_decoding.py (demo 4), for MI355X. The workgroups
+ * (batch * kv_heads * ceil(group / 8) * num_splits) run in rounds of
+ * min(num_cus, remaining); a round costs a fixed workgroup time plus its
+ * largest segment's K/V bytes at a per-byte time that grows with the number
+ * of workgroups streaming at once; unequal lengths take the average load
+ * plus the largest segment (list-scheduling bound). The constants were
+ * fitted to measured MI355X calls (relative RMS error 4.7 %). Same
+ * arguments as fd_plan_splits; returns a negative value on bad arguments.
+ */
+double fd_plan_time_us(int batch, int heads, int kv_heads, int dim, int dtype,
+                       const int32_t* seqlens_host, int num_cus, int num_splits);
 
 /*
  * fd_workspace_bytes -- size of the workspace for a call with these

@@ -352,3 +352,39 @@ def test_kv_layout_strides():
     assert (lay.batch_stride, lay.head_stride, lay.token_stride) == (4 * 80 * 64, 80 * 64, 64)
     with pytest.raises(ValueError):
         fd.kv_layout(torch.zeros(3, 4, 64, 50).transpose(2, 3), "bhsd")
+
+
+def _model(B, H, Hkv, L, ns, cus=256, D=128, dtype=fd.FD_F16):
+    return fd.fd_plan_time_us(B, H, Hkv, D, dtype, L if isinstance(L, list) else [L] * B, ns,
+                              num_cus=cus)
+
+
+@pytest.mark.parametrize("B,H,Hkv,L", [(1, 16, 2, 65536), (8, 16, 2, 8192), (64, 16, 2, 2048),
+                                       (16, 32, 8, 131072), (1, 32, 8, 8192), (3, 28, 4, 40000)])
+def test_planner_takes_the_least_modelled_time(B, H, Hkv, L):
+    ns = plan(B, H, Hkv, 128, [L] * B)
+    cap = min(math.ceil(L / 256), L)
+    times = {n: _model(B, H, Hkv, L, n) for n in range(1, cap + 1)}
+    assert times[ns] == min(times.values())
+    assert all(times[n] > times[ns] for n in range(1, ns))   # ties go to fewer splits
+
+
+def test_time_model_shows_demo4_wave_quantisation():
+    # 04_flash_decoding.py, demo 4: too few splits leave compute units idle
+    # (time falls as splits are added until one round fills the device),
+    # beyond that more splits only add rounds and combine work
+    t = [_model(8, 16, 2, 8192, n) for n in (1, 2, 4, 8, 16, 32, 64, 128)]
+    assert t[0] > t[1] > t[2] > t[3] > t[4]        # 16 .. 256 workgroups
+    assert t[4] == min(t) and t[7] > t[5] > t[4]
+    # single launch for one split: no combine term; two splits add it
+    one, two = _model(64, 16, 2, 2048, 1), _model(64, 16, 2, 2048, 2)
+    assert one > two   # 128 workgroups leave half the device idle
+    # bytes scale the time: twice the keys, about twice the streaming part
+    assert _model(16, 32, 8, 65536, 2) > 1.9 * _model(16, 32, 8, 32768, 2) - 10
+
+
+def test_time_model_argument_errors():
+    with pytest.raises(ValueError):
+        _model(1, 32, 8, 1000, 0)
+    with pytest.raises(ValueError):
+        fd.fd_plan_time_us(1, 30, 8, 128, fd.FD_F16, [100], 1, num_cus=256)
