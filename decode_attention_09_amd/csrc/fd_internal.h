@@ -104,8 +104,8 @@ struct CombineArgs {
 
 // Launchers (defined in fd_split_<dtype>.hip and fd_combine.hip). They
 // return the hipError_t of the launch.
-// `mfma` selects the matrix-core QK^T kernel where one exists (16-bit
-// inputs, head dim 128); otherwise the VALU kernel runs.
+// `mfma` selects the matrix-core QK^T kernel where one exists (head dim
+// 128); otherwise the VALU kernel runs.
 hipError_t launch_split_f32(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,
                             hipStream_t s);
 hipError_t launch_split_f16(const SplitArgs& a, int dim, int rows, bool mfma, dim3 grid,

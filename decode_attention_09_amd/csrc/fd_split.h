@@ -40,6 +40,14 @@
 //  * Register tile pipeline: the loads of the next kPrefetchTilesValu
 //    (kPrefetchTilesMfma) tiles are in flight while the current tile is
 //    computed.
+//  * The matrix-core kernel (split_kernel_mfma, head dim 128, every dtype)
+//    computes QK^T on v_mfma_f32_16x16x32_{f16,bf16} / v_mfma_f32_16x16x4_f32
+//    with the group's query rows as the 16 MFMA columns; see its section.
+//  * Schedules: one workgroup per segment, or (QUEUE instances) a grid of
+//    one workgroup per compute unit whose workgroups claim further segments
+//    from a counter once their first one is done (claim_next).
+//  * Single launch: with an arrival-counter array, the last of a unit's
+//    workgroups merges the unit's partials itself (arrive_and_merge).
 #pragma once
 
 #include <type_traits>
