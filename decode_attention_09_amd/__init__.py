@@ -20,7 +20,7 @@ __all__ = [
     "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
     "fd_decode_attention_unnorm", "workspace_views_unnorm", "fd_decode_attention_noalloc",
     "FD_NOALLOC_SCRATCH_BYTES", "fd_set_schedule", "FD_SCHED_AUTO", "FD_SCHED_STATIC",
-    "FD_SCHED_QUEUE", "fd_set_combine", "FD_COMBINE_SEPARATE", "FD_COMBINE_FUSED",
+    "FD_SCHED_QUEUE", "FD_SCHED_STEAL", "fd_set_combine", "FD_COMBINE_SEPARATE", "FD_COMBINE_FUSED",
     "fd_plan_time_us",
 ]
 
@@ -28,7 +28,7 @@ FD_F32, FD_F16, FD_BF16 = 0, 1, 2
 FD_MAX_SPLITS = 16384
 FD_NOALLOC_SCRATCH_BYTES = 16 << 20
 FD_PATH_AUTO, FD_PATH_VALU, FD_PATH_MFMA, FD_PATH_UNPACKED = 0, 1, 2, 3
-FD_SCHED_AUTO, FD_SCHED_STATIC, FD_SCHED_QUEUE = 0, 1, 2
+FD_SCHED_AUTO, FD_SCHED_STATIC, FD_SCHED_QUEUE, FD_SCHED_STEAL = 0, 1, 2, 3
 FD_COMBINE_SEPARATE, FD_COMBINE_FUSED = 0, 1
 _STATUS = {0: "FD_OK", 1: "FD_ERR_INVALID_ARG", 2: "FD_ERR_UNSUPPORTED",
            3: "FD_ERR_EMPTY_SPLIT", 4: "FD_ERR_HIP", 5: "FD_ERR_SCRATCH"}
@@ -136,8 +136,10 @@ def fd_set_kernel_path(path: int) -> int:
 
 def fd_set_schedule(sched: int) -> int:
     """Select how split launches from this thread hand segments to
-    workgroups (FD_SCHED_AUTO / _STATIC / _QUEUE); returns the previous
-    setting. The results are bitwise identical under every schedule."""
+    workgroups (FD_SCHED_AUTO / _STATIC / _QUEUE / _STEAL); returns the
+    previous setting. Static and queue results are bitwise identical; the
+    steal schedule (whole calls only) merges other key ranges, so its
+    results differ by rounding."""
     prev = load_library().fd_set_schedule(int(sched))
     if prev < 0:
         raise ValueError(f"unknown schedule {sched}")

@@ -219,12 +219,14 @@ struct Workspace {
   float* lbuf = nullptr;
   int* queue = nullptr;     // claim counter (normalised format)
   int* arrivals = nullptr;  // arrival counters of fused calls (normalised format)
+  unsigned long long* steal = nullptr;  // share words of the steal schedule (normalised format)
 };
 
 constexpr size_t kQueueBytes = 256;
+constexpr size_t kStealBytes = (size_t)fd::kStealMaxShares * sizeof(unsigned long long);
 
 size_t control_bytes(int batch, int heads) {
-  return kQueueBytes + align256((size_t)batch * heads * sizeof(int));
+  return kQueueBytes + align256((size_t)batch * heads * sizeof(int)) + kStealBytes;
 }
 
 size_t workspace_bytes(Format f, int batch, int heads, int dim, int num_splits) {
@@ -245,6 +247,9 @@ Workspace workspace_views(Format f, void* base, int batch, int heads, int dim, i
     w.lse = reinterpret_cast<float*>(ws + opart);
     w.queue = reinterpret_cast<int*>(ws + opart + align256(rows * sizeof(float)));
     w.arrivals = reinterpret_cast<int*>(ws + opart + align256(rows * sizeof(float)) + kQueueBytes);
+    w.steal = reinterpret_cast<unsigned long long*>(
+        ws + opart + align256(rows * sizeof(float)) + kQueueBytes +
+        align256((size_t)batch * heads * sizeof(int)));
   } else {
     w.mbuf = reinterpret_cast<float*>(ws + opart);
     w.lbuf = reinterpret_cast<float*>(ws + opart + align256(rows * sizeof(float)));
@@ -262,6 +267,35 @@ Workspace workspace_views(Format f, void* base, int batch, int heads, int dim, i
 // device, so the host cannot tell the cases apart: callers with ragged
 // batches select FD_SCHED_QUEUE.
 bool use_queue(int sched) { return sched == FD_SCHED_QUEUE; }
+
+// Target chunks per share of the steal schedule (each chunk at least
+// fd::kStealMinChunk keys, so shorter shares have fewer). Measured on
+// MI355X, Llama B16/128K (bf16, 8 slots: 2 shares per unit, 3 steal slots
+// each), whole call in graph replay, static schedule at the planner's 2
+// splits 1295-1330 us on that device: 1 chunk (no claims) 1281-1285 us,
+// 4: 1281, 16: 1262-1269, 32: 1239-1240, 64: 1237-1239.
+#ifndef FD_STEAL_CHUNKS
+#define FD_STEAL_CHUNKS 32
+#endif
+constexpr int kStealChunks = FD_STEAL_CHUNKS;
+// Steal slots per share in the planner's layout for the steal schedule.
+constexpr int kStealPlanCap = 3;
+
+// Shares per unit of a steal-scheduled call: the largest divisor d of
+// num_splits with at most one workgroup per compute unit (units * d <= cus)
+// and num_splits / d - 1 steal slots per share in 1..kStealMaxCap; 0 if
+// none (the call then runs the static schedule).
+int steal_shares_per_unit(int units, int num_splits, int cus) {
+  for (int d = num_splits / 2; d >= 1; --d) {
+    if (num_splits % d != 0) continue;
+    const int cap = num_splits / d - 1;
+    if (cap < 1 || cap > fd::kStealMaxCap) continue;
+    if ((int64_t)units * d > cus) continue;
+    if ((int64_t)units * d > fd::kStealMaxShares) continue;
+    return d;
+  }
+  return 0;
+}
 
 int launch_split(const void* q, const void* k, const void* v, const int32_t* cu, int batch,
                  int heads, int kv_heads, int dim, int num_splits, float scale, Format fmt,
@@ -308,12 +342,34 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
   a.arrivals = fused ? w.arrivals : nullptr;
   a.queue = !fused && w.queue != nullptr && a.kv_nt && use_queue(sched) ? w.queue
                                                                                    : nullptr;
+  dim3 grid((unsigned)sz.workgroups);
+  const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
+  // Steal schedule: whole calls in the normalised format on the
+  // matrix-core kernel; one workgroup per share, non-temporal loads.
+  a.steal = nullptr;
+  a.steal_nsh = a.steal_cap = a.steal_chunks = a.steal_shares = 0;
+  if (sched == FD_SCHED_STEAL && !fused && !direct && fmt == kNormalised && mfma && dim == 128 &&
+      w.steal != nullptr) {
+    const int units = batch * kv_heads * sz.row_chunks;
+    const int d = steal_shares_per_unit(units, num_splits, cus);
+    if (d > 0) {
+      a.steal = w.steal;
+      a.steal_nsh = d;
+      a.steal_cap = num_splits / d - 1;
+      a.steal_chunks = kStealChunks;
+      a.steal_shares = units * d;
+      a.queue = nullptr;
+      a.kv_nt = 1;
+      a.wide = 0;
+      grid = dim3((unsigned)a.steal_shares);
+      const hipError_t er = fd::launch_steal_reset(a.steal, a.steal_shares, stream);
+      if (er != hipSuccess) return hip_fail(er, "steal reset launch");
+    }
+  }
   if (a.queue != nullptr) {
     const hipError_t er = fd::launch_queue_reset(a.queue, stream);
     if (er != hipSuccess) return hip_fail(er, "queue reset launch");
   }
-  dim3 grid((unsigned)sz.workgroups);
-  const bool mfma = path == FD_PATH_MFMA || (path == FD_PATH_AUTO && auto_mfma(dtype, dim, sz.group));
   hipError_t e;
   switch (dtype) {
     case FD_F32: e = fd::launch_split_f32(a, dim, sz.rows, mfma, grid, stream); break;
@@ -327,7 +383,7 @@ int launch_split(const void* q, const void* k, const void* v, const int32_t* cu,
 int split_impl(Format fmt, const void* q, const void* k, const void* v,
                const int32_t* cu_seqlens_k, int batch, int heads, int kv_heads, int dim,
                int num_splits, float scale, void* workspace, void* stream, int dtype,
-               const fd_kv_layout* layout) {
+               const fd_kv_layout* layout, int sched) {
   const int path = g_path;
   Sizes sz;
   int st = check_common(batch, heads, kv_heads, dim, num_splits, dtype, &sz, rows_per_pass(path));
@@ -342,7 +398,7 @@ int split_impl(Format fmt, const void* q, const void* k, const void* v,
   const Workspace w = workspace_views(fmt, workspace, batch, heads, dim, num_splits);
   return launch_split(q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale, fmt,
                       w, nullptr, 0, static_cast<hipStream_t>(stream), dtype, L, sz, path,
-                      g_sched);
+                      sched);
 }
 
 int combine_impl(Format fmt, const void* workspace, int batch, int heads, int dim,
@@ -411,7 +467,7 @@ int attention_impl(Format fmt, const void* q, const void* k, const void* v,
                         fmt, w, out, 0, s, dtype, L, sz, path, FD_SCHED_STATIC, true);
   }
   st = split_impl(fmt, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits, scale,
-                  workspace, stream, dtype, layout);
+                  workspace, stream, dtype, layout, g_sched);
   if (st != FD_OK) return st;
   return combine_impl(fmt, workspace, batch, heads, dim, num_splits, out, stream, dtype);
 }
@@ -528,6 +584,19 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
       choice = (int)ns;
     }
   }
+  // Under the steal schedule, a call that can take it (matrix-core kernel,
+  // head dim 128) and whose longest sequence gives every share two chunks
+  // or more gets the steal layout instead: as many shares per unit as fit
+  // one per compute unit, each with kStealPlanCap steal slots.
+  const bool mfma = g_path == FD_PATH_MFMA ||
+                    (g_path == FD_PATH_AUTO && auto_mfma(dtype, dim, p.sz.group));
+  if (g_sched == FD_SCHED_STEAL && mfma && dim == 128) {
+    int64_t nsh = p.units < p.cus ? p.cus / p.units : 1;
+    const int64_t slots = nsh * (1 + kStealPlanCap);
+    if (slots <= max_splits && p.units * nsh <= fd::kStealMaxShares &&
+        p.max_len / nsh >= 2 * fd::kStealMinChunk)
+      choice = (int)slots;
+  }
   *num_splits_out = choice;
   return FD_OK;
 }
@@ -546,7 +615,7 @@ int fd_decode_split(const void* q, const void* k, const void* v, const int32_t* 
                     int batch, int heads, int kv_heads, int dim, int num_splits, float scale,
                     void* workspace, void* stream, int dtype, const fd_kv_layout* layout) {
   return split_impl(kNormalised, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
-                    scale, workspace, stream, dtype, layout);
+                    scale, workspace, stream, dtype, layout, g_sched);
 }
 
 int fd_decode_combine(const void* workspace, int batch, int heads, int dim, int num_splits,
@@ -567,7 +636,7 @@ int fd_decode_split_unnorm(const void* q, const void* k, const void* v,
                            int dim, int num_splits, float scale, void* workspace, void* stream,
                            int dtype, const fd_kv_layout* layout) {
   return split_impl(kUnnorm, q, k, v, cu_seqlens_k, batch, heads, kv_heads, dim, num_splits,
-                    scale, workspace, stream, dtype, layout);
+                    scale, workspace, stream, dtype, layout, g_sched);
 }
 
 int fd_decode_combine_unnorm(const void* workspace, int batch, int heads, int dim,
@@ -632,7 +701,9 @@ int fd_set_combine(int mode) {
 }
 
 int fd_set_schedule(int sched) {
-  if (sched != FD_SCHED_AUTO && sched != FD_SCHED_STATIC && sched != FD_SCHED_QUEUE) return -1;
+  if (sched != FD_SCHED_AUTO && sched != FD_SCHED_STATIC && sched != FD_SCHED_QUEUE &&
+      sched != FD_SCHED_STEAL)
+    return -1;
   const int prev = g_sched;
   g_sched = sched;
   return prev;

@@ -218,6 +218,19 @@ hipError_t launch_queue_reset(int* queue, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void steal_reset_kernel(unsigned long long* words, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    words[i] = 0ull;
+}
+
+hipError_t launch_steal_reset(unsigned long long* words, int n, hipStream_t s) {
+  const int block = 256;
+  const int grid = n > 0 ? (n + block - 1) / block : 1;
+  hipLaunchKernelGGL(steal_reset_kernel, dim3(grid < 64 ? grid : 64), dim3(block), 0, s, words,
+                     n);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s) {
   switch (dtype) {
     case DT_F32: return launch_combine_dt<DT_F32>(a, dim, s);

@@ -58,6 +58,14 @@ constexpr int valu_loads_per_tile(int elem_bytes, int dim) {
 constexpr int kPrefetchTilesValu = FD_PREFETCH_TILES_VALU;
 constexpr int kPrefetchTilesMfma = FD_PREFETCH_TILES_MFMA;
 
+// Steal schedule limits: steal slots per share (a 4-bit field of the share
+// word) and share words in the workspace's control block.
+constexpr int kStealMaxCap = 15;
+constexpr int kStealMaxShares = 4096;
+// Smallest chunk (keys) of the steal schedule: an owner's claim runs a
+// whole chunk ahead of its use, so its round trip is hidden.
+constexpr int kStealMinChunk = 512;
+
 // Arguments of the split kernel (passed by value).
 struct SplitArgs {
   const void* q;
@@ -90,6 +98,18 @@ struct SplitArgs {
   // num_splits workgroups to arrive merges the unit's partials into `out`
   // and sets the counter back to zero. nullptr: the combine kernel merges.
   int* arrivals;
+  // Steal schedule (matrix-core kernel, whole calls in the normalised
+  // format): the keys of each unit are cut into steal_nsh proportional
+  // shares, one workgroup each (the grid); share r owns the partial slots
+  // r * (1 + steal_cap) .. r * (1 + steal_cap) + steal_cap of its unit
+  // (num_splits = steal_nsh * (1 + steal_cap)). Its workgroup streams its
+  // share in chunks claimed ahead from its word in `steal` (zero at launch),
+  // one partial for the run it streamed; workgroups that are done take the
+  // back half of the unclaimed chunks of another share (at most steal_cap
+  // times per share), one partial each. steal_chunks: chunks per share.
+  // nullptr: off.
+  unsigned long long* steal;
+  int steal_nsh, steal_cap, steal_chunks, steal_shares;
 };
 
 struct CombineArgs {
@@ -115,5 +135,7 @@ hipError_t launch_split_bf16(const SplitArgs& a, int dim, int rows, bool mfma, d
 hipError_t launch_combine(const CombineArgs& a, int dtype, int dim, hipStream_t s);
 // Zeroes the claim counter of a queue-scheduled split launch (one thread).
 hipError_t launch_queue_reset(int* queue, hipStream_t s);
+// Zeroes the n share words of a steal-scheduled split launch.
+hipError_t launch_steal_reset(unsigned long long* words, int n, hipStream_t s);
 
 }  // namespace fd

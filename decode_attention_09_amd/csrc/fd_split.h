@@ -50,6 +50,7 @@
 //    workgroups merges the unit's partials itself (arrive_and_merge).
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "fd_internal.h"
@@ -337,39 +338,31 @@ struct Segment {
   uint32_t tsb;    // bytes between consecutive keys
 };
 
-// The sequence, its varlen bounds and the proportional segment
-// [L*s/ns, L*(s+1)/ns) (64-bit products) of an item.
+// The sequence of an item (b) and its cu_seqlens_k bounds.
+__device__ __forceinline__ void sequence_of(const SeqTable& st, const WorkItem& w,
+                                            const LaneSeqs& ls, int& b, int& cu0, int& cu1) {
+  if (st.batch <= kLptMaxBatch) {
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(ls.rank == w.rank);
+    b = hit ? (int)__builtin_ctzll(hit) : w.rank;
+    cu0 = __builtin_amdgcn_readlane(ls.lo, b);
+    cu1 = __builtin_amdgcn_readlane(ls.hi, b);
+  } else {
+    b = w.rank;
+    cu0 = st.cu[b];
+    cu1 = st.cu[b + 1];
+  }
+}
+
+// Keys [seg0, seg1) of sequence b (first key row cu0) for an item.
 template <int EB>
-__device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const SeqTable& st,
-                                                  const WorkItem& w, const LaneSeqs& ls) {
+__device__ __forceinline__ Segment segment_at(const SplitArgs& a, const WorkItem& w, int b,
+                                              int cu0, int64_t seg0, int64_t seg1) {
   Segment g;
+  g.b = b;
   g.sid = w.sid;
   g.kvh = w.kvh;
   g.h0 = w.h0;
   g.nrows = w.nrows;
-  int cu0, cu1;
-  if (st.batch <= kLptMaxBatch) {
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(ls.rank == w.rank);
-    g.b = hit ? (int)__builtin_ctzll(hit) : w.rank;
-    cu0 = __builtin_amdgcn_readlane(ls.lo, g.b);
-    cu1 = __builtin_amdgcn_readlane(ls.hi, g.b);
-  } else {
-    g.b = w.rank;
-    cu0 = st.cu[g.b];
-    cu1 = st.cu[g.b + 1];
-  }
-  const int ns = a.num_splits;
-  const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
-  int64_t seg0, seg1;
-  if (a.ceil_bounds) {
-    // ceil-equal: size = ceil(L/ns) from sid*size, cut at L (may be empty)
-    const int64_t size = (L + ns - 1) / ns;
-    seg0 = min(size * g.sid, L);
-    seg1 = min(size * g.sid + size, L);
-  } else {
-    seg0 = L * g.sid / ns;
-    seg1 = L * (g.sid + 1) / ns;
-  }
   g.nkeys = seg1 - seg0;
   const int64_t row0 =
       (int64_t)g.b * a.sb + (int64_t)cu0 * a.scu + (int64_t)g.kvh * a.sh + seg0 * a.st;
@@ -377,6 +370,29 @@ __device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const SeqT
   g.v = static_cast<const char*>(a.v) + row0 * EB;
   g.tsb = (uint32_t)(a.st * EB);
   return g;
+}
+
+// The sequence, its varlen bounds and the proportional segment
+// [L*s/ns, L*(s+1)/ns) (64-bit products) of an item.
+template <int EB>
+__device__ __forceinline__ Segment locate_segment(const SplitArgs& a, const SeqTable& st,
+                                                  const WorkItem& w, const LaneSeqs& ls) {
+  int b, cu0, cu1;
+  sequence_of(st, w, ls, b, cu0, cu1);
+  const int ns = a.num_splits;
+  const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
+  const int sid = w.sid;
+  int64_t seg0, seg1;
+  if (a.ceil_bounds) {
+    // ceil-equal: size = ceil(L/ns) from sid*size, cut at L (may be empty)
+    const int64_t size = (L + ns - 1) / ns;
+    seg0 = min(size * sid, L);
+    seg1 = min(size * sid + size, L);
+  } else {
+    seg0 = L * sid / ns;
+    seg1 = L * (sid + 1) / ns;
+  }
+  return segment_at<EB>(a, w, b, cu0, seg0, seg1);
 }
 
 // Descriptors for tile j of TK keys of a segment: sized to end at the last
@@ -532,6 +548,150 @@ __device__ __forceinline__ int claim_next(const SplitArgs& a, int& slot) {
   return slot;
 }
 
+// ------------------------------------------------------ steal schedule --
+// Work stealing at chunk granularity for launches whose workgroups stream
+// equal amounts at unequal rates (on MI355X the XCDs of one launch finish
+// their equal segments up to 20 % apart, and workgroups on one XCD differ
+// too). Share r of a unit is the proportional key range
+// [L*r/nsh, L*(r+1)/nsh), cut into nc chunks of ck keys (the last one
+// shorter). Its workgroup (the owner) streams chunk 0 at once and claims
+// chunks 1, 2, ... one at a time, each claim issued a chunk ahead, so its
+// run [0, n) is one contiguous stream with one partial. A workgroup whose
+// run is over takes, from the share with the most unclaimed chunks, the
+// back half of them (a thief's run, one partial in the next steal slot of
+// that share). Each chunk goes to exactly one run: both sides update the
+// share's word with one atomic operation, the owner from the front and a
+// thief from the back, and the owner's claim and a thief's take only chunks
+// below the back count and above the front count of the word value they
+// replace. Nobody waits for another workgroup: a claim or a take that finds
+// nothing ends that part of the walk.
+//
+// Share word (64 bits): chunks the owner claimed after its first (bits
+// 0-19), chunks taken from the back (20-39), steals (40-43), and the
+// share's chunk count (44-63, published with the owner's first claim; 0
+// until then, which makes the share look empty).
+constexpr int kStealBackShift = 20;
+constexpr int kStealCountShift = 40;
+constexpr int kStealChunksShift = 44;
+constexpr unsigned long long kStealField = (1ull << 20) - 1;
+constexpr int kStealKeyQuantum = 64;       // chunk keys: a multiple of one tile per wave
+constexpr int kStealScans = 64;            // victim searches per workgroup, at most
+
+// Schedules of the matrix-core kernel (template argument).
+constexpr int kSchedStatic = 0, kSchedQueue = 1, kSchedSteal = 2;
+
+__device__ __forceinline__ int steal_front(unsigned long long w) { return (int)(w & kStealField); }
+__device__ __forceinline__ int steal_back(unsigned long long w) {
+  return (int)((w >> kStealBackShift) & kStealField);
+}
+__device__ __forceinline__ int steal_count(unsigned long long w) {
+  return (int)((w >> kStealCountShift) & 15ull);
+}
+__device__ __forceinline__ int steal_chunks(unsigned long long w) {
+  return (int)(w >> kStealChunksShift);
+}
+// Chunks of a share no run has taken yet (negative once it is exhausted).
+__device__ __forceinline__ int steal_unclaimed(unsigned long long w) {
+  return steal_chunks(w) - 1 - steal_front(w) - steal_back(w);
+}
+
+struct Share {
+  int64_t start, len, ck;  // first key, keys, keys per chunk
+  int nc;                  // chunks (>= 1)
+};
+
+// Share r of nsh of a sequence of L keys, in about `chunks` chunks of a
+// multiple of kStealKeyQuantum keys (at most `chunks`, which the host keeps
+// below 2^20 - 2, so the word's fields cannot overflow).
+__device__ __forceinline__ Share share_of(int64_t L, int r, int nsh, int chunks) {
+  Share s;
+  s.start = L * r / nsh;
+  s.len = L * (r + 1) / nsh - s.start;
+  const int64_t per = (s.len + chunks - 1) / chunks;
+  s.ck = (per + kStealKeyQuantum - 1) / kStealKeyQuantum * kStealKeyQuantum;
+  if (s.ck < kStealMinChunk) s.ck = kStealMinChunk;
+  const int64_t n = (s.len + s.ck - 1) / s.ck;
+  s.nc = n > 0 ? (int)n : 1;
+  return s;
+}
+
+// A slot of no run: zero output and LSE -inf (ignored by the merge).
+template <int D, int NW>
+__device__ __forceinline__ void store_empty(const SplitArgs& a, const Segment& sg, int sid) {
+  constexpr int Q = D / 4;
+  const int ns = a.num_splits;
+  for (int idx = threadIdx.x; idx < sg.nrows * Q; idx += NW * kWave) {
+    const int g = idx / Q;
+    const int d = (idx % Q) * 4;
+    const int h = sg.h0 + g;
+    const int64_t row = ((int64_t)sg.b * a.heads + h) * ns + sid;
+    *reinterpret_cast<f4_t*>(a.opart + row * D + d) = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (d == 0) a.lse[((int64_t)sg.b * ns + sid) * a.heads + h] = kNegInf;
+  }
+}
+
+// A thief's run: share, chunks [c0, c1), steal slot index (share < 0: none).
+struct StealJob {
+  int share, c0, c1, slot;
+};
+
+// One victim search and take by the whole workgroup (it synchronises; `job`
+// is LDS for the broadcast). Returns share -1 when no share has two or more
+// unclaimed chunks and a free steal slot, share -2 when the take lost a race
+// (search again). Relaxed atomics suffice: the words pass no data, and the
+// partials are read by the next launch.
+template <int NW>
+__device__ __forceinline__ StealJob steal_search(const SplitArgs& a, StealJob& job,
+                                                 unsigned (&red)[NW]) {
+  const int tid = threadIdx.x;
+  // best key: unclaimed chunks (high bits), then the lowest share
+  unsigned key = 0;
+  for (int v = tid; v < a.steal_shares; v += NW * kWave) {
+    const unsigned long long w =
+        __hip_atomic_load(a.steal + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int u = steal_unclaimed(w);
+    if (u >= 2 && steal_count(w) < a.steal_cap) {
+      const unsigned k = ((unsigned)u << 12) | (unsigned)(kStealMaxShares - 1 - v);
+      key = k > key ? k : key;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned o = __shfl_xor(key, off, kWave);
+    key = o > key ? o : key;
+  }
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned best = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) best = red[w] > best ? red[w] : best;
+    StealJob j{-1, 0, 0, 0};
+    if (best != 0) {
+      const int v = kStealMaxShares - 1 - (int)(best & 4095u);
+      unsigned long long* word = a.steal + v;
+      unsigned long long w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      j.share = -2;
+      const int u = steal_unclaimed(w);
+      if (u >= 2 && steal_count(w) < a.steal_cap) {
+        const int m = u / 2;  // the back half; the owner keeps the front one
+        const unsigned long long want =
+            w + ((unsigned long long)m << kStealBackShift) + (1ull << kStealCountShift);
+        if (__hip_atomic_compare_exchange_strong(word, &w, want, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          const int n = steal_chunks(w), bk = steal_back(w);
+          j = StealJob{v, n - bk - m, n - bk, steal_count(w)};
+        }
+      }
+    }
+    job = j;
+  }
+  __syncthreads();
+  const StealJob j = job;
+  __syncthreads();  // every thread has its copy before the next search writes
+  return j;
+}
+
 // ------------------------------------------------------------ pipeline --
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -549,9 +709,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // return zeros without touching memory; skipping them costs registers);
 // the walk stops after the last tile. The
 // scheduling barriers keep each prefetch ahead of the compute it overlaps.
-template <int PF, int NW, typename Tile, typename Load, typename Compute>
-__device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF + 1], Load&& load,
-                                              Compute&& compute) {
+// hook(j) runs before each tile's step (before the load of tile j + PF*NW)
+// and may extend nt.
+template <int PF, int NW, typename Tile, typename Load, typename Compute, typename Hook>
+__device__ __forceinline__ void tile_pipeline(int first, const int& nt, Tile (&buf)[PF + 1],
+                                              Load&& load, Compute&& compute, Hook&& hook) {
   if (first >= nt) return;  // uniform: this wave has no tile of the segment
   static_for<PF - 1>([&](auto ui) {
     constexpr int u = decltype(ui)::value + 1;
@@ -563,6 +725,7 @@ __device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF 
     static_for<PF + 1>([&](auto ui) {
       constexpr int u = decltype(ui)::value;
       if (!done) {
+        hook(j);
         load(j + PF * NW, buf[(u + PF) % (PF + 1)]);
         __builtin_amdgcn_sched_barrier(0);
         compute(j, buf[u]);
@@ -573,6 +736,12 @@ __device__ __forceinline__ void tile_pipeline(int first, int nt, Tile (&buf)[PF 
     });
     if (done) break;
   }
+}
+
+template <int PF, int NW, typename Tile, typename Load, typename Compute>
+__device__ __forceinline__ void tile_pipeline(int first, const int& nt, Tile (&buf)[PF + 1],
+                                              Load&& load, Compute&& compute) {
+  tile_pipeline<PF, NW, Tile>(first, nt, buf, load, compute, [](int) {});
 }
 
 // --------------------------------------------------------- VALU kernel --
@@ -813,7 +982,7 @@ __device__ __forceinline__ f4_t mfma_qk(const u4_t& k, const u4_t& q, f4_t acc) 
                                                    __builtin_bit_cast(b8_t, q), acc, 0, 0, 0);
 }
 
-template <int DT, int GC, bool NT, bool QUEUE>
+template <int DT, int GC, bool NT, int SCH>
 __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int32_t* cu, int batch, SplitArgs a) {
   static_assert(GC <= 16, "one 16-column MFMA tile of query rows");
   constexpr bool F32 = DT == DT_F32;
@@ -997,10 +1166,32 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
   Tile buf[kPrefetchTilesMfma + 1];
   __shared__ int sm_next;
   int item = blockIdx.x;
+  // steal schedule: the current run, first the owner's of share blockIdx.x
+  StealJob job{(int)blockIdx.x, 0, 1, 0};
+  bool owner = true;
+  [[maybe_unused]] int searches = 0;
+  __shared__ int sm_claim[2];
+  __shared__ int sm_steals;
+  __shared__ StealJob sm_job;
+  __shared__ unsigned sm_red[NW];
   while (true) {
+    if constexpr (SCH == kSchedSteal) {
+      const int unit = job.share / a.steal_nsh, r = job.share % a.steal_nsh;
+      item = unit * a.num_splits + r * (1 + a.steal_cap) + (owner ? 0 : 1 + job.slot);
+    }
     const WorkItem wi = decode_item<GC>(a, item);
     load_q(wi, wi.rank);  // guess: sequence == rank (equal lengths)
-    sg = locate_segment<EB>(a, st, wi, ls);
+    [[maybe_unused]] Share sh{};
+    if constexpr (SCH == kSchedSteal) {
+      int b, cu0, cu1;
+      sequence_of(st, wi, ls, b, cu0, cu1);
+      const int64_t L = cu1 > cu0 ? (int64_t)cu1 - cu0 : 0;
+      sh = share_of(L, job.share % a.steal_nsh, a.steal_nsh, a.steal_chunks);
+      sg = segment_at<EB>(a, wi, b, cu0, sh.start + (int64_t)job.c0 * sh.ck,
+                          sh.start + min((int64_t)job.c1 * sh.ck, sh.len));
+    } else {
+      sg = locate_segment<EB>(a, st, wi, ls);
+    }
     if (sg.b != wi.rank) load_q(wi, sg.b);
     load_tile_of(sg, wave, buf[0]);
     m_run = kNegInf;
@@ -1010,8 +1201,53 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
     for (int g = 0; g < GC; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
-    const int nt = (int)((sg.nkeys + TK - 1) / TK);
-    tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+    int nt = (int)((sg.nkeys + TK - 1) / TK);
+    if constexpr (SCH == kSchedSteal) {
+      // The owner's run grows a chunk at a time. Thread 0 claims chunk
+      // `owned` a chunk ahead; at the step before any wave would load a tile
+      // of that chunk (every wave has tpw steps per full chunk), it
+      // publishes the result, and the workgroup extends the run or ends it.
+      // The barrier sits at the same step of every wave, and every chunk
+      // before the last one is full, so every wave reaches it.
+      unsigned long long pending = 0;  // thread 0: word value its claim returns
+      int parity = 0;
+      const int tpw = (int)(sh.ck / (TK * NW));
+      int hook_step = owner && sh.nc >= 2 ? tpw - kPrefetchTilesMfma : INT_MAX;
+      unsigned long long* const word = a.steal + job.share;
+      if (owner && tid == 0) {
+        sm_steals = 0;
+        if (sh.nc >= 2)  // claims chunk 1 and publishes the chunk count
+          pending = __hip_atomic_fetch_add(
+              word, 1ull + ((unsigned long long)sh.nc << kStealChunksShift), __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+      }
+      auto grow = [&](int j) {
+        if ((j - wave) / NW != hook_step) return;  // uniform
+        if (tid == 0) {
+          const int chunk = 1 + steal_front(pending);
+          const bool ok = chunk < sh.nc - steal_back(pending);
+          sm_steals = steal_count(pending);  // final once the claims end
+          sm_claim[parity] = ok ? chunk : -1;
+          if (ok && chunk + 1 < sh.nc)
+            pending = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const int got = sm_claim[parity];  // two slots: the next write is two barriers away
+        parity ^= 1;
+        if (got >= 0) {
+          const int owned = got + 1;
+          sg.nkeys = min((int64_t)owned * sh.ck, sh.len);
+          nt = (int)((sg.nkeys + TK - 1) / TK);
+          hook_step = owned < sh.nc ? hook_step + tpw : INT_MAX;
+        } else {
+          hook_step = INT_MAX;
+        }
+      };
+      tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile, grow);
+    } else {
+      tile_pipeline<kPrefetchTilesMfma, NW, Tile>(wave, nt, buf, load_tile, compute_tile);
+    }
 
     // ---- merge the four key groups R of this wave onto its true max ----
     const float M = across_groups<16>(m_true, OpMax{});
@@ -1049,12 +1285,25 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
     }
     __syncthreads();
     store_segment<DT, D, GC, NW>(a, sg, sm_m, sm_l, sm_acc);
-    if constexpr (!QUEUE) {  // static schedule: the loop body runs once
+    if constexpr (SCH == kSchedStatic) {  // the loop body runs once
       if (a.arrivals != nullptr) arrive_and_merge<DT, D, NW>(a, sg, item / a.num_splits, sm_next);
       break;
+    } else if constexpr (SCH == kSchedQueue) {
+      item = claim_next(a, sm_next);
+      if (item >= a.items) break;
+    } else {
+      if (owner) {  // steal slots no thief took: empty partials
+        const int taken = sm_steals;
+        for (int s = 1 + taken; s <= a.steal_cap; ++s) store_empty<D, NW>(a, sg, sg.sid + s);
+        owner = false;
+      }
+      StealJob j;
+      do {
+        j = steal_search<NW>(a, sm_job, sm_red);
+      } while (j.share == -2 && ++searches < kStealScans);
+      if (j.share < 0 || ++searches > kStealScans) break;
+      job = j;
     }
-    item = claim_next(a, sm_next);
-    if (item >= a.items) break;
   }
 }
 
@@ -1063,12 +1312,12 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
 // kMfmaWorkgroupsPerCu matrix-core workgroups reside on one compute unit
 // (0 if the device's per-workgroup limit does not allow it). Computed once
 // per kernel instance.
-template <int DT, int GC, bool NT, bool QUEUE>
+template <int DT, int GC, bool NT, int SCH>
 size_t mfma_lds_reserve() {
   static const size_t bytes = [] {
     hipFuncAttributes fa;
     if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
-                                      &split_kernel_mfma<DT, GC, NT, QUEUE>)) != hipSuccess) {
+                                      &split_kernel_mfma<DT, GC, NT, SCH>)) != hipSuccess) {
       (void)hipGetLastError();
       return (size_t)0;
     }
@@ -1117,19 +1366,19 @@ dim3 queue_grid(const SplitArgs& a, const void* kernel, int block, size_t lds) {
   return dim3((unsigned)(g < (long)a.items ? g : (long)a.items));
 }
 
-template <int DT, int GC, bool NT, bool QUEUE>
+template <int DT, int GC, bool NT, int SCH>
 struct MfmaTag {};
 template <int DT, int D, int GC, bool NT, int NW, bool QUEUE>
 struct ValuTag {};
 
-template <int DT, int GC, bool NT, bool QUEUE>
+template <int DT, int GC, bool NT, int SCH>
 hipError_t launch_mfma(const SplitArgs& a, dim3 grid, hipStream_t s) {
   const dim3 block(kWave * kWavesMfma);
-  const size_t lds = mfma_lds_reserve<DT, GC, NT, QUEUE>();
-  if constexpr (QUEUE)
-    grid = queue_grid<MfmaTag<DT, GC, NT, QUEUE>>(
-        a, reinterpret_cast<const void*>(&split_kernel_mfma<DT, GC, NT, QUEUE>), block.x, lds);
-  hipLaunchKernelGGL((split_kernel_mfma<DT, GC, NT, QUEUE>), grid, block, lds, s, a.cu, a.batch,
+  const size_t lds = mfma_lds_reserve<DT, GC, NT, SCH>();
+  if constexpr (SCH == kSchedQueue)
+    grid = queue_grid<MfmaTag<DT, GC, NT, SCH>>(
+        a, reinterpret_cast<const void*>(&split_kernel_mfma<DT, GC, NT, SCH>), block.x, lds);
+  hipLaunchKernelGGL((split_kernel_mfma<DT, GC, NT, SCH>), grid, block, lds, s, a.cu, a.batch,
                      a);
   return hipGetLastError();
 }
@@ -1169,7 +1418,8 @@ hipError_t launch_split_dnq(const SplitArgs& a, int rows, bool mfma, dim3 grid, 
   if constexpr (D == 128) {
     if (mfma)
       return by_rows(rows, [&](auto r) {
-        return launch_mfma<DT, decltype(r)::value, NT, QUEUE>(a, grid, s);
+        return launch_mfma<DT, decltype(r)::value, NT, QUEUE ? kSchedQueue : kSchedStatic>(
+            a, grid, s);
       });
   }
   if constexpr (!NT && !QUEUE) {
@@ -1185,8 +1435,19 @@ hipError_t launch_split_dnq(const SplitArgs& a, int rows, bool mfma, dim3 grid, 
 
 // The queue schedule is only taken by launches that fill the device (which
 // always carry non-temporal K/V loads); the host never asks for it elsewhere.
+// The steal schedule exists in the matrix-core kernel; the host asks for it
+// only there (grid: one workgroup per share).
 template <int DT, int D>
 hipError_t launch_split_d(const SplitArgs& a, int rows, bool mfma, dim3 grid, hipStream_t s) {
+  if (a.steal != nullptr) {
+    if constexpr (D == 128) {
+      if (mfma)
+        return by_rows(rows, [&](auto r) {
+          return launch_mfma<DT, decltype(r)::value, true, kSchedSteal>(a, grid, s);
+        });
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.queue != nullptr && a.kv_nt)
     return launch_split_dnq<DT, D, true, true>(a, rows, mfma, grid, s);
   return a.kv_nt ? launch_split_dnq<DT, D, true, false>(a, rows, mfma, grid, s)

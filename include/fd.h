@@ -116,7 +116,12 @@ typedef struct fd_kv_layout {
  * 256 keys per split; decode_attention_splitkv.py's non-empty rule): among
  * split counts that leave every split >= 1 key and the longest sequence
  * >= 256 keys per split, take the one with the least modelled call time
- * (fd_plan_time_us). Ties go to fewer splits.
+ * (fd_plan_time_us). Ties go to fewer splits. When the calling thread's
+ * schedule is FD_SCHED_STEAL (fd_set_schedule) and the call would run the
+ * matrix-core kernel (head dim 128), the result is instead the steal
+ * layout's partial-slot count, nsh * 4 with nsh = max(1, num_cus / units)
+ * shares per unit (units = batch * kv_heads * ceil(group / 8)), provided
+ * the longest sequence gives every share at least 1024 keys.
  * Returns FD_ERR_EMPTY_SPLIT if some length is < 1, FD_ERR_INVALID_ARG for
  * bad sizes, FD_ERR_HIP if the device query fails.
  */
@@ -151,12 +156,15 @@ double fd_plan_time_us(int batch, int heads, int kv_heads, int dim, int dtype,
  *                                           (fd_set_schedule), then int32
  *                                           [batch*heads] arrival counters of
  *                                           fused calls (fd_set_combine),
- *                                           padded to a multiple of 256 bytes
+ *                                           padded to a multiple of 256 bytes,
+ *                                           then 4096 uint64 share words of a
+ *                                           steal-scheduled call
  * LSE starts at the first 256-byte boundary after Opart, the control block
  * at the first 256-byte boundary after LSE. The shapes follow part_shape /
  * lse_shape of decode_attention_splitkv.py, in fp32. Its contents before a
  * call do not matter, except for the arrival counters of a fused call,
- * which must be zero (a queue-scheduled call zeroes its own counter).
+ * which must be zero (queue- and steal-scheduled calls zero their own
+ * counter and words with a kernel launched just before the split launch).
  */
 size_t fd_workspace_bytes(int batch, int heads, int num_splits, int dim);
 
@@ -286,13 +294,30 @@ int fd_set_kernel_path(int path);
  * launched just before, on the same stream), so compute units that stream
  * faster process more segments. FD_SCHED_AUTO (the default): the library's
  * measured choice. The segments, their bounds and every partial are the
- * same under all schedules, so the results are bitwise identical; the
- * queue applies to launches with a normalised-format workspace
- * (fd_decode_attention with a workspace, fd_decode_attention_noalloc,
- * fd_decode_split) and is ignored elsewhere. Returns the previous
+ * same under the static and queue schedules, so their results are bitwise
+ * identical; the queue applies to launches with a normalised-format
+ * workspace (fd_decode_attention with a workspace,
+ * fd_decode_attention_noalloc, fd_decode_split) and is ignored elsewhere.
+ * FD_SCHED_STEAL (normalised-format launches on the matrix-core kernel
+ * with num_splits > 1; others run the static schedule): the keys of each
+ * (sequence, KV
+ * head) unit are cut into nsh proportional shares, one workgroup each,
+ * where nsh is the largest divisor of num_splits <= num_splits / 2 with
+ * units * nsh <= the device's compute units and cap = num_splits / nsh - 1
+ * in 1..15 (none: static schedule). Share r owns partial slots
+ * r*(1+cap) .. r*(1+cap)+cap. Its workgroup streams the share in chunks it
+ * claims one ahead from the share's word; a workgroup that is done takes
+ * the back half of the unclaimed chunks of the share that has the most,
+ * up to cap times per share, each take one partial in the next slot; slots
+ * no run used hold LSE -inf and zeros. The same attention, but the key
+ * ranges merged depend on timing, so results vary by rounding between
+ * calls. The partials fd_decode_split leaves are then these slots, not
+ * the proportional splits; fd_decode_combine merges them alike (a
+ * fused-combine call runs the static schedule). fd_plan_splits gives the
+ * slot count. Returns the previous
  * setting, or -1 (unchanged) for an unknown value.
  */
-enum { FD_SCHED_AUTO = 0, FD_SCHED_STATIC = 1, FD_SCHED_QUEUE = 2 };
+enum { FD_SCHED_AUTO = 0, FD_SCHED_STATIC = 1, FD_SCHED_QUEUE = 2, FD_SCHED_STEAL = 3 };
 int fd_set_schedule(int sched);
 
 /*

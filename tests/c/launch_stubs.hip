@@ -19,5 +19,6 @@ hipError_t launch_combine(const CombineArgs&, int, int, hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_queue_reset(int*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_steal_reset(unsigned long long*, int, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace fd

@@ -63,8 +63,9 @@ def test_workspace_bytes_layout(B, H, D, ns):
     lse_off = (opart + 255) // 256 * 256
     ctl_off = lse_off + (B * ns * H * 4 + 255) // 256 * 256
     # control block: the queue's claim counter (256 B), then B*H arrival
-    # counters of fused calls padded to 256 B
-    assert n == ctl_off + 256 + (B * H * 4 + 255) // 256 * 256
+    # counters of fused calls padded to 256 B, then the steal schedule's
+    # 4096 64-bit share words
+    assert n == ctl_off + 256 + (B * H * 4 + 255) // 256 * 256 + 4096 * 8
 
 
 @pytest.mark.parametrize("B,H,D,ns", [(1, 8, 128, 7), (4, 32, 16, 16), (3, 5, 64, 1000)])
@@ -388,3 +389,30 @@ def test_time_model_argument_errors():
         _model(1, 32, 8, 1000, 0)
     with pytest.raises(ValueError):
         fd.fd_plan_time_us(1, 30, 8, 128, fd.FD_F16, [100], 1, num_cus=256)
+
+
+def test_planner_gives_the_steal_layout_under_the_steal_schedule():
+    # under FD_SCHED_STEAL: shares per unit = CUs / units (at least 1), each
+    # with 3 steal slots, where the matrix-core kernel runs (head dim 128,
+    # group >= 2 or the matrix-core path forced) and every share of the
+    # longest sequence has >= 1024 keys; otherwise the static plan
+    static = {key: plan(*key[:4], [key[4]] * key[0], dtype=fd.FD_BF16)
+              for key in ((16, 32, 8, 128, 1024), (16, 32, 8, 64, 131072),
+                          (16, 32, 32, 128, 131072))}
+    prev = fd.fd_set_schedule(fd.FD_SCHED_STEAL)
+    try:
+        assert plan(16, 32, 8, 128, [131072] * 16, dtype=fd.FD_BF16) == 8   # 128 units: 2 shares
+        assert plan(1, 32, 8, 128, [131072], dtype=fd.FD_BF16) == 128       # 8 units: 32 shares
+        assert plan(64, 32, 8, 128, [8192] * 64, dtype=fd.FD_BF16) == 4     # 512 units: 1 share
+        assert plan(16, 32, 8, 128, [131072] * 16, cus=128, dtype=fd.FD_BF16) == 4
+        # shares of 512 keys, head dim 64, MHA (VALU kernel): the static plan
+        for key, ns in static.items():
+            assert plan(*key[:4], [key[4]] * key[0], dtype=fd.FD_BF16) == ns
+        prev_path = fd.fd_set_kernel_path(fd.FD_PATH_VALU)
+        try:   # the VALU kernel has no steal schedule
+            valu_steal = plan(16, 32, 8, 128, [131072] * 16, dtype=fd.FD_BF16)
+        finally:
+            fd.fd_set_kernel_path(prev_path)
+    finally:
+        fd.fd_set_schedule(prev)
+    assert valu_steal == plan(16, 32, 8, 128, [131072] * 16, dtype=fd.FD_BF16) != 8

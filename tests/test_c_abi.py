@@ -39,14 +39,18 @@ def test_c_program(c_program):
     assert st == "0" and 1 <= int(ns) <= 16
     assert out["plan_empty"] == "3"
     rows = 2 * 8 * 4
+    # control block: claim counter 256 B, arrival counters padded to 256 B,
+    # 4096 share words of the steal schedule
+    steal = 4096 * 8
     assert int(out["ws"]) == ((rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
-                              + 256 + 256)
+                              + 256 + 256 + steal)
     assert int(out["ws_unnorm"]) == ((rows * 128 * 4 + 255) // 256 * 256
                                      + (rows * 4 + 255) // 256 * 256 + rows * 4)
     assert out["ws_bad"] == "0"
     # (batch, heads, num_splits, dim): 128 splits at dim 64, then 64 splits at dim 128
     a, b = (int(x) for x in out["ws_order"].split())
-    assert a == 128 * 64 * 4 + 512 + 512 and b == 64 * 128 * 4 + 256 + 512 and a != b
+    assert a == 128 * 64 * 4 + 512 + 512 + steal and b == 64 * 128 * 4 + 256 + 512 + steal
+    assert a != b
     a, b = (int(x) for x in out["ws_unnorm_order"].split())
     assert a == 128 * 64 * 4 + 2 * 128 * 4 and b == 64 * 128 * 4 + 256 + 64 * 4
     assert out["null_args"] == "1"
