@@ -2,8 +2,8 @@
 group size, KV heads, batch, ragged lengths (empty sequences and lengths
 below the split count included), split count, K/V layout (packed,
 [B, Hkv, S, D], [B, S, Hkv, D]), split format, kernel path, sometimes a
-non-default scale, the single-launch (fused) combine and the queue
-schedule, and checks every output element against the fp64
+non-default scale, the single-launch (fused) combine and the queue or
+steal schedule, and checks every output element against the fp64
 oracle's direct attention (empty sequences: zero rows). K/V rows outside
 the sequences are NaN, so an over-read shows.
 
@@ -73,7 +73,8 @@ def _draw(i: int):
     scale = None if rng.random() < 0.6 else float(rng.uniform(-1.0, 2.0))
     # drawn last, so the draws above are those of the sweep without them
     combine = "fused" if rng.random() < 0.35 else "separate"
-    sched = "queue" if rng.random() < 0.35 else "auto"
+    u = rng.random()
+    sched = "queue" if u < 0.35 else "steal" if u < 0.6 else "auto"
     return dict(dtype=dtype, dim=dim, group=group, kv_heads=kv_heads, lengths=lengths, ns=ns,
                 layout=layout, fmt=fmt, path=path, scale=scale, combine=combine, sched=sched,
                 seed=i)
@@ -109,7 +110,8 @@ def test_random_case_matches_oracle(c):
     prev = fd.fd_set_kernel_path(PATHS[c["path"]])
     prev_c = fd.fd_set_combine(fd.FD_COMBINE_FUSED if c["combine"] == "fused"
                                else fd.FD_COMBINE_SEPARATE)
-    prev_s = fd.fd_set_schedule(fd.FD_SCHED_QUEUE if c["sched"] == "queue" else fd.FD_SCHED_AUTO)
+    prev_s = fd.fd_set_schedule({"queue": fd.FD_SCHED_QUEUE, "steal": fd.FD_SCHED_STEAL,
+                                 "auto": fd.FD_SCHED_AUTO}[c["sched"]])
     try:
         out = call(inp.q, k, v, inp.cu_seqlens_k, c["ns"], scale=scale, layout=c["layout"])
         torch.cuda.synchronize()

@@ -189,6 +189,36 @@ def test_steal_matches_oracle(case):
     check_workspace(inp, ns, ws)
 
 
+def _random_case(i):
+    """A seeded draw that takes the steal schedule: head dim 128, group
+    2..16, ragged lengths up to 40,000 keys (empty ones included), a split
+    count with a valid share layout, any dtype and K/V layout."""
+    rng = np.random.default_rng(7100 + i)
+    dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    group = int(rng.choice([2, 3, 4, 5, 7, 8, 9, 12, 16]))
+    kv_heads = int(rng.integers(1, 9))
+    batch = int(rng.integers(1, 9))
+    lengths = [0 if rng.random() < 0.1 else int(rng.integers(1, 40001)) for _ in range(batch)]
+    if max(lengths) == 0:
+        lengths[0] = 20000
+    layout = str(rng.choice(["packed", "bhsd"]))
+    units = batch * kv_heads * -(-group // 8)
+    choices = [ns for ns in range(2, 65) if shares_per_unit(units, ns, _cus()) > 0]
+    ns = int(rng.choice(choices))
+    w = W.Workload(f"steal_r{i}", batch, group * kv_heads, kv_heads, 128, dtype, kv_len=None,
+                   layout=layout)
+    return w, lengths, ns
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_steal_random_draws(i):
+    w, lengths, ns = _random_case(i)
+    inp = W.make_inputs(w, H.DEV, seed=100 + i, lengths=lengths, pad_rows=4)
+    out, ws = steal_call(inp, ns)
+    check_vs_oracle(inp, out)
+    check_workspace(inp, ns, ws)
+
+
 def test_steal_takes_work_from_long_shares():
     """One long sequence among short ones: the short shares end at once and
     their workgroups take chunks of the long shares."""
