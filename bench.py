@@ -304,6 +304,8 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
                    "kv_heads": w.kv_heads, "head_dim": w.dim, "kv_len_total": sum(inp.lengths),
                    "layout": w.layout, "num_splits": ns,
                    "partials": "(m, l, acc), ceil-equal bounds" if unnorm
+                   else "(o_s, lse_s), runs of chunks within proportional shares"
+                   if schedule == "steal" and not single_launch
                    else "(o_s, lse_s), proportional bounds",
                    "schedule": schedule,
                    "split_workgroups": split_workgroups(
