@@ -77,10 +77,13 @@ def workload_by_name(name: str):
 
 # Schedule per workload where one other than the library's default is
 # measured faster (A/B in one process on MI355X, whole calls in graph
-# replay): the steal schedule on the largest Llama point, 1295-1330 us ->
-# 1237-1240 us per call (at its planner layout of 8 partial slots against
-# the static schedule's planned 2 splits).
-BENCH_SCHEDULE = {"llama8b_b16_l131072_h32kv8_d128_bf16": "steal"}
+# replay): the steal schedule on the largest Llama point, 1283-1332 us ->
+# 1233-1240 us per call on devices with a wide XCD spread, level elsewhere
+# (at its planner layout of 8 partial slots against the static schedule's
+# planned 2 splits); the queue schedule on the ragged varlen batch (the one
+# the library's documentation recommends it for), 201.9 -> 187.2 us per call.
+BENCH_SCHEDULE = {"llama8b_b16_l131072_h32kv8_d128_bf16": "steal",
+                  "varlen_qwen7b_b32_h28kv4_d128_f16": "queue"}
 
 
 def set_schedule(fd, w, requested):
