@@ -98,18 +98,58 @@ def test_llama_long_context(batch, kv_len):
     if batch * kv_len <= 16 * 8192:
         check_full(inp, ns)
     else:
-        out = H.host(H.gpu_attention(inp, ns))
-        assert np.isfinite(out).all()
-        pairs = [(b, j) for b in range(batch) for j in range(w.kv_heads)]
-        refs = H.oracle_pairs(inp, pairs, workers=8)
-        worst = 0.0
-        for (b, j), ref in refs.items():
-            err = H.max_err(out[b, j * 4:(j + 1) * 4], ref)
-            worst = max(worst, err)
-            assert err <= H.TOL["bf16"], (b, j, err)
-        print(f"  {w.name} ns={ns}: {len(pairs)} pairs, max_abs_err={worst:.3e}", flush=True)
+        check_every_pair(inp, ns)
     del inp
     torch.cuda.empty_cache()
+
+
+def check_every_pair(inp, ns):
+    """Every (sequence, KV head) pair of a whole call against the oracle, its
+    K/V rows copied to the host one pair at a time."""
+    w = inp.workload
+    G = w.group
+    out = H.host(H.gpu_attention(inp, ns))
+    assert np.isfinite(out).all()
+    pairs = [(b, j) for b in range(w.batch) for j in range(w.kv_heads)]
+    refs = H.oracle_pairs(inp, pairs, workers=8)
+    worst = 0.0
+    for (b, j), ref in refs.items():
+        err = H.max_err(out[b, j * G:(j + 1) * G], ref)
+        worst = max(worst, err)
+        assert err <= H.TOL[w.dtype], (b, j, err)
+    print(f"  {w.name} ns={ns}: {len(pairs)} pairs, max_abs_err={worst:.3e}", flush=True)
+
+
+def test_bench_line_under_the_steal_schedule():
+    """The bench line as the benchmark times it: Llama B16 x 131,072 keys
+    under the steal schedule, the planner's steal layout (8 slots on 256
+    CUs), every (sequence, KV head) pair against the oracle."""
+    fd = H.fd()
+    w = W.llama(16, 131072)
+    inp = W.make_inputs(w, H.DEV)
+    prev = fd.fd_set_schedule(fd.FD_SCHED_STEAL)
+    try:
+        ns = fd.fd_plan_splits(w.batch, w.heads, w.kv_heads, w.dim, fd.FD_BF16, inp.lengths)
+        H.announce("steal layout", ns)
+        assert ns > 2
+        check_every_pair(inp, ns)
+    finally:
+        fd.fd_set_schedule(prev)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_varlen_under_the_queue_schedule():
+    """The varlen workload as the benchmark times it: the queue schedule,
+    ns=8, against the oracle."""
+    fd = H.fd()
+    w = W.varlen_qwen()
+    inp = W.make_inputs(w, H.DEV)
+    prev = fd.fd_set_schedule(fd.FD_SCHED_QUEUE)
+    try:
+        check_full(inp, W.varlen_splits(w, inp.lengths))
+    finally:
+        fd.fd_set_schedule(prev)
 
 
 @pytest.mark.parametrize("path", ["valu", "mfma"])
