@@ -43,9 +43,12 @@
 //  * The matrix-core kernel (split_kernel_mfma, head dim 128, every dtype)
 //    computes QK^T on v_mfma_f32_16x16x32_{f16,bf16} / v_mfma_f32_16x16x4_f32
 //    with the group's query rows as the 16 MFMA columns; see its section.
-//  * Schedules: one workgroup per segment, or (QUEUE instances) a grid of
+//  * Schedules: one workgroup per segment; (queue instances) a grid of
 //    one workgroup per compute unit whose workgroups claim further segments
-//    from a counter once their first one is done (claim_next).
+//    from a counter once their first one is done (claim_next); or (steal
+//    instances of the matrix-core kernel) one workgroup per share of each
+//    unit, streaming its share in chunks claimed ahead and then taking the
+//    unclaimed back half of other shares (steal_search).
 //  * Single launch: with an arrival-counter array, the last of a unit's
 //    workgroups merges the unit's partials itself (arrive_and_merge).
 #pragma once
@@ -559,12 +562,14 @@ __device__ __forceinline__ int claim_next(const SplitArgs& a, int& slot) {
 // run [0, n) is one contiguous stream with one partial. A workgroup whose
 // run is over takes, from the share with the most unclaimed chunks, the
 // back half of them, rounded up (a thief's run, one partial in the next
-// steal slot of that share). Each chunk goes to exactly one run: both sides update the
-// share's word with one atomic operation, the owner from the front and a
-// thief from the back, and the owner's claim and a thief's take only chunks
-// below the back count and above the front count of the word value they
-// replace. Nobody waits for another workgroup: a claim or a take that finds
-// nothing ends that part of the walk.
+// steal slot of that share). Each chunk goes to exactly one run: both
+// sides update the share's word with one atomic operation, the owner from
+// the front and a thief from the back; an owner's claim succeeds only below
+// the back count of the word value it replaces, a take only covers chunks
+// above the front count of the value it replaces, so whichever comes first
+// bounds the other. The owner claims until a claim fails, so the front and
+// back runs meet. Nobody waits for another workgroup: a claim or a take
+// that finds nothing ends that part of the walk.
 //
 // Share word (64 bits): chunks the owner claimed after its first (bits
 // 0-19), chunks taken from the back (20-39), steals (40-43), and the
