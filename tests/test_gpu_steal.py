@@ -347,3 +347,55 @@ def test_share_layout_rule():
     if cus == 256:
         assert shares_per_unit(128, 8, cus) == 2
         assert shares_per_unit(8, 128, cus) == 32
+
+
+def test_schedule_is_per_thread():
+    """Two threads calling at the same time, one under the static schedule
+    and one under the steal schedule, each with its own stream and
+    workspace: the static thread's outputs equal a static call bitwise and
+    its share words stay zero; the steal thread's words show its shares'
+    published chunk counts and its outputs match the oracle."""
+    import threading
+    fd = H.fd()
+    w = W.Workload("thr", 3, 32, 4, 128, "bf16", kv_len=None)
+    inp = W.make_inputs(w, H.DEV, seed=33, lengths=[5000, 3000, 4100])
+    ns = 8
+    n = fd.fd_workspace_bytes(w.batch, w.heads, ns, w.dim)
+    prev = fd.fd_set_schedule(fd.FD_SCHED_STATIC)
+    ref = fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns)
+    fd.fd_set_schedule(prev)
+    torch.cuda.synchronize()
+    got, errors = {}, []
+    gate = threading.Barrier(2)
+
+    def worker(name, sched):
+        try:
+            fd.fd_set_schedule(sched)
+            s = torch.cuda.Stream()
+            ws = torch.zeros(n, dtype=torch.uint8, device=H.DEV)
+            outs = []
+            gate.wait()
+            for _ in range(10):
+                outs.append(fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns,
+                                                   workspace=ws, stream=s))
+            s.synchronize()
+            got[name] = (outs, ws)
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=("static", fd.FD_SCHED_STATIC)),
+          threading.Thread(target=worker, args=("steal", fd.FD_SCHED_STEAL))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    _, _, steal_off = _offsets(w, ns)
+    outs, ws = got["static"]
+    assert all(torch.equal(o, ref) for o in outs)
+    assert not ws[steal_off:].any()
+    outs, ws = got["steal"]
+    check_workspace(inp, ns, ws)
+    assert ws[steal_off:].any()
+    for o in outs:
+        check_vs_oracle(inp, o)
