@@ -345,6 +345,10 @@ FIT_SWEEPS = [
     ("llama8b_b16_l8192_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
     ("llama8b_b1_l8192_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
     ("llama8b_b16_l1024_h32kv8_d128_bf16", [1, 2, 4, 8, 16, 32, 64, 128]),
+    ("llama8b_b1_l131072_h32kv8_d128_bf16", [8, 16, 24, 32, 48, 64, 96, 128, 192, 256]),
+    ("llama8b_b1_l32768_h32kv8_d128_bf16", [8, 16, 24, 32, 48, 64, 96, 128, 192]),
+    ("fd_ubench_b1_l131072_h16kv2_d128_f16", [16, 32, 48, 64, 96, 128, 192, 256]),
+    ("llama8b_b16_l32768_h32kv8_d128_bf16", [1, 2, 3, 4, 6, 8]),
 ]
 
 
