@@ -399,3 +399,22 @@ def test_schedule_is_per_thread():
     assert ws[steal_off:].any()
     for o in outs:
         check_vs_oracle(inp, o)
+
+
+def test_noalloc_entry_point_under_the_steal_schedule():
+    """fd_decode_attention_noalloc runs the steal schedule on the static
+    scratch's control block: two calls in a row (the second smaller) match
+    the oracle."""
+    fd = H.fd()
+    prev = fd.fd_set_schedule(fd.FD_SCHED_STEAL)
+    try:
+        for lengths, seed in (([20000, 9000, 15000], 51), ([6000, 3000], 52)):
+            w = W.Workload("noalloc_steal", len(lengths), 16, 4, 128, "f16", kv_len=None)
+            inp = W.make_inputs(w, H.DEV, seed=seed, lengths=lengths)
+            out = torch.empty_like(inp.q)
+            H.announce("noalloc steal", lengths)
+            fd.fd_decode_attention_noalloc(inp.q, inp.k, inp.v, inp.cu_seqlens_k, 8, out)
+            torch.cuda.synchronize()
+            check_vs_oracle(inp, out)
+    finally:
+        fd.fd_set_schedule(prev)
