@@ -46,7 +46,7 @@ DEFAULT_WORKLOAD = "llama8b_b16_l131072_h32kv8_d128_bf16"
 PEAK_GBS = 8000.0
 LLC_BYTES = 256 * 2 ** 20       # MI355X Infinity Cache (MALL)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fd_split.h", "fd_internal.h"]
+KERNEL_SOURCES = ["fd_split.h", "fd_internal.h", "fd_steal.h"]
 
 
 def _code_only(text: str) -> str:

@@ -20,6 +20,7 @@
 
 #include "../../include/fd.h"
 #include "fd_internal.h"
+#include "fd_steal.h"
 
 // Partials of fd_decode_attention_noalloc: one array per GPU, resident from
 // module load until the process ends. In host code `scratch` names a host-side
@@ -278,6 +279,8 @@ bool use_queue(int sched) { return sched == FD_SCHED_QUEUE; }
 #define FD_STEAL_CHUNKS 32
 #endif
 constexpr int kStealChunks = FD_STEAL_CHUNKS;
+static_assert(kStealChunks >= 1 && kStealChunks <= fd::kStealMaxChunks,
+              "the share word's front and back counts hold at most kStealMaxChunks");
 // Steal slots per share in the planner's layout for the steal schedule.
 constexpr int kStealPlanCap = 3;
 

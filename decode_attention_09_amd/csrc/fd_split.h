@@ -57,6 +57,7 @@
 #include <type_traits>
 
 #include "fd_internal.h"
+#include "fd_steal.h"
 
 namespace fd {
 
@@ -571,34 +572,12 @@ __device__ __forceinline__ int claim_next(const SplitArgs& a, int& slot) {
 // back runs meet. Nobody waits for another workgroup: a claim or a take
 // that finds nothing ends that part of the walk.
 //
-// Share word (64 bits): chunks the owner claimed after its first (bits
-// 0-19), chunks taken from the back (20-39), steals (40-43), and the
-// share's chunk count (44-63, published with the owner's first claim; 0
-// until then, which makes the share look empty).
-constexpr int kStealBackShift = 20;
-constexpr int kStealCountShift = 40;
-constexpr int kStealChunksShift = 44;
-constexpr unsigned long long kStealField = (1ull << 20) - 1;
+// The share word and the arithmetic of claims and takes are in fd_steal.h.
 constexpr int kStealKeyQuantum = 64;       // chunk keys: a multiple of one tile per wave
 constexpr int kStealScans = 64;            // victim searches per workgroup, at most
 
 // Schedules of the matrix-core kernel (template argument).
 constexpr int kSchedStatic = 0, kSchedQueue = 1, kSchedSteal = 2;
-
-__device__ __forceinline__ int steal_front(unsigned long long w) { return (int)(w & kStealField); }
-__device__ __forceinline__ int steal_back(unsigned long long w) {
-  return (int)((w >> kStealBackShift) & kStealField);
-}
-__device__ __forceinline__ int steal_count(unsigned long long w) {
-  return (int)((w >> kStealCountShift) & 15ull);
-}
-__device__ __forceinline__ int steal_chunks(unsigned long long w) {
-  return (int)(w >> kStealChunksShift);
-}
-// Chunks of a share no run has taken yet (negative once it is exhausted).
-__device__ __forceinline__ int steal_unclaimed(unsigned long long w) {
-  return steal_chunks(w) - 1 - steal_front(w) - steal_back(w);
-}
 
 struct Share {
   int64_t start, len, ck;  // first key, keys, keys per chunk
@@ -655,7 +634,7 @@ __device__ __forceinline__ StealJob steal_search(const SplitArgs& a, StealJob& j
     const unsigned long long w =
         __hip_atomic_load(a.steal + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int u = steal_unclaimed(w);
-    if (u >= 1 && steal_count(w) < a.steal_cap) {
+    if (steal_take(w, a.steal_cap).m > 0) {
       const unsigned k = ((unsigned)u << 12) | (unsigned)(kStealMaxShares - 1 - v);
       key = k > key ? k : key;
     }
@@ -677,22 +656,15 @@ __device__ __forceinline__ StealJob steal_search(const SplitArgs& a, StealJob& j
       unsigned long long* word = a.steal + v;
       unsigned long long w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       j.share = -2;
-      const int u = steal_unclaimed(w);
-      if (u >= 1 && steal_count(w) < a.steal_cap) {
-        // the back half, rounded up: the owner keeps the front one plus the
-        // chunk it is streaming, so even its last unclaimed chunk is worth
-        // taking (measured on MI355X, Llama B16/128K at 8 slots: taking only
-        // from two or more unclaimed chunks, the floor half, 1240-1242 us;
-        // this rule 1233-1235 us)
-        const int m = (u + 1) / 2;
-        const unsigned long long want =
-            w + ((unsigned long long)m << kStealBackShift) + (1ull << kStealCountShift);
-        if (__hip_atomic_compare_exchange_strong(word, &w, want, __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          const int n = steal_chunks(w), bk = steal_back(w);
-          j = StealJob{v, n - bk - m, n - bk, steal_count(w)};
-        }
-      }
+      // the back half, rounded up: even a last unclaimed chunk is worth
+      // taking (measured on MI355X, Llama B16/128K at 8 slots: taking only
+      // from two or more unclaimed chunks, the floor half, 1240-1242 us;
+      // this rule 1233-1235 us)
+      const StealTake tk = steal_take(w, a.steal_cap);
+      if (tk.m > 0 &&
+          __hip_atomic_compare_exchange_strong(word, &w, tk.want, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        j = StealJob{v, tk.c0, tk.c1, tk.slot};
     }
     job = j;
   }
@@ -1227,19 +1199,17 @@ __global__ __launch_bounds__(kWave* kWavesMfma) void split_kernel_mfma(const int
       if (owner && tid == 0) {
         sm_steals = 0;
         if (sh.nc >= 2)  // claims chunk 1 and publishes the chunk count
-          pending = __hip_atomic_fetch_add(
-              word, 1ull + ((unsigned long long)sh.nc << kStealChunksShift), __ATOMIC_RELAXED,
-              __HIP_MEMORY_SCOPE_AGENT);
+          pending = __hip_atomic_fetch_add(word, steal_first_claim(sh.nc), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
       }
       auto grow = [&](int j) {
         if ((j - wave) / NW != hook_step) return;  // uniform
         if (tid == 0) {
-          const int chunk = 1 + steal_front(pending);
-          const bool ok = chunk < sh.nc - steal_back(pending);
+          const int chunk = steal_claimed_chunk(pending, sh.nc);
           sm_steals = steal_count(pending);  // final once the claims end
-          sm_claim[parity] = ok ? chunk : -1;
-          if (ok && chunk + 1 < sh.nc)
-            pending = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED,
+          sm_claim[parity] = chunk;
+          if (chunk >= 0 && chunk + 1 < sh.nc)
+            pending = __hip_atomic_fetch_add(word, kStealClaim, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
