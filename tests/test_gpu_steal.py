@@ -210,7 +210,7 @@ def _random_case(i):
     return w, lengths, ns
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(24))
 def test_steal_random_draws(i):
     w, lengths, ns = _random_case(i)
     inp = W.make_inputs(w, H.DEV, seed=100 + i, lengths=lengths, pad_rows=4)
