@@ -431,7 +431,12 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # Untimed calls before the timed ones. On MI355X the first tens of
+    # milliseconds of back-to-back calls run slower (the bench line: first 25
+    # calls ~1470 us on average, then 1233-1238 us; on another device ~80
+    # calls at ~1285 us before ~1236 us), so the default warm-up spans
+    # ~0.12 s of the bench line.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true",
                     help="one line per workload (no CPU leg unless --cpu-seconds is given)")
