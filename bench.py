@@ -75,24 +75,28 @@ def workload_by_name(name: str):
                      + ", ".join(w.name for w in W.all_workloads()))
 
 
-# Schedule per workload where one other than the library's default is
-# measured faster (A/B in one process on MI355X, whole calls in graph
-# replay): the steal schedule on the largest Llama point, 1283-1332 us ->
-# 1233-1240 us per call on devices with a wide XCD spread, level elsewhere
-# (at its planner layout of 8 partial slots against the static schedule's
-# planned 2 splits); the queue schedule on the ragged varlen batch (the one
-# the library's documentation recommends it for), 201.9 -> 187.2 us per call.
-BENCH_SCHEDULE = {"llama8b_b16_l131072_h32kv8_d128_bf16": "steal",
-                  "varlen_qwen7b_b32_h28kv4_d128_f16": "queue"}
+# Schedule for workloads whose split count the pages fix, where the
+# library's planner does not choose: the queue schedule on the ragged varlen
+# batch at its 8 splits (the header's advice for ragged batches; A/B in one
+# process on MI355X, whole calls in graph replay: 201.9 -> 187.2 us).
+BENCH_SCHEDULE = {"varlen_qwen7b_b32_h28kv4_d128_f16": "queue"}
 
 
-def set_schedule(fd, w, requested):
-    """Set the calling thread's schedule for workload w (the requested one,
-    else BENCH_SCHEDULE's, else the library's) before its split count is
-    planned; returns its name."""
-    name = requested or BENCH_SCHEDULE.get(w.name, "auto")
-    fd.fd_set_schedule({"auto": fd.FD_SCHED_AUTO, "static": fd.FD_SCHED_STATIC,
-                        "queue": fd.FD_SCHED_QUEUE, "steal": fd.FD_SCHED_STEAL}[name])
+def set_schedule(fd, w, requested, ns_override=0):
+    """Set the calling thread's schedule for workload w before its split
+    count is planned: the requested one, else BENCH_SCHEDULE's, else, where
+    the planner picks the split count, fd_plan_schedule's recommendation,
+    else the library's default. Returns its name."""
+    code = {"auto": fd.FD_SCHED_AUTO, "static": fd.FD_SCHED_STATIC,
+            "queue": fd.FD_SCHED_QUEUE, "steal": fd.FD_SCHED_STEAL}
+    name = requested or BENCH_SCHEDULE.get(w.name)
+    if name is None and w.num_splits is None and not ns_override and w.kv_len is not None:
+        lengths = [w.kv_len] * w.batch
+        dt = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}[w.dtype]
+        sched, _ = fd.fd_plan_schedule(w.batch, w.heads, w.kv_heads, w.dim, dt, lengths)
+        name = {v: k for k, v in code.items()}[sched]
+    name = name or "auto"
+    fd.fd_set_schedule(code[name])
     return name
 
 
@@ -501,7 +505,7 @@ def main():
                     for ns in splits]
         cpu_s = args.cpu_seconds or 0.0
         for w, ns in todo:
-            sched = set_schedule(fd, w, args.schedule)
+            sched = set_schedule(fd, w, args.schedule, ns)
             r = run(w, args.steps, args.warmup, cpu_s, ns_override=ns, rows_per_workgroup=rows,
                     fmt=args.format, graph=args.graph, schedule=sched)
             r["kernel_path"] = args.kernel_path
@@ -512,7 +516,7 @@ def main():
         return
     cpu_s = 10.0 if args.cpu_seconds is None else args.cpu_seconds
     w = workload_by_name(args.workload)
-    sched = set_schedule(fd, w, args.schedule)
+    sched = set_schedule(fd, w, args.schedule, args.num_splits)
     r = run(w, args.steps, args.warmup, cpu_s, ns_override=args.num_splits,
             rows_per_workgroup=rows, fmt=args.format, graph=args.graph, schedule=sched)
     r["kernel_path"] = args.kernel_path

@@ -19,7 +19,7 @@ __all__ = [
     "FD_PATH_AUTO", "FD_PATH_VALU", "FD_PATH_MFMA", "FD_PATH_UNPACKED", "workspace_views",
     "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
     "fd_decode_attention_unnorm", "workspace_views_unnorm", "fd_decode_attention_noalloc",
-    "FD_NOALLOC_SCRATCH_BYTES", "fd_set_schedule", "FD_SCHED_AUTO", "FD_SCHED_STATIC",
+    "FD_NOALLOC_SCRATCH_BYTES", "fd_set_schedule", "fd_plan_schedule", "FD_SCHED_AUTO", "FD_SCHED_STATIC",
     "FD_SCHED_QUEUE", "FD_SCHED_STEAL", "fd_set_combine", "FD_COMBINE_SEPARATE", "FD_COMBINE_FUSED",
     "fd_plan_time_us",
 ]
@@ -75,6 +75,10 @@ def load_library():
     lib.fd_plan_splits.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), i32,
                                    i32, ctypes.POINTER(ctypes.c_int)]
     lib.fd_plan_splits.restype = i32
+    lib.fd_plan_schedule.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32),
+                                     i32, i32, ctypes.POINTER(ctypes.c_int),
+                                     ctypes.POINTER(ctypes.c_int)]
+    lib.fd_plan_schedule.restype = i32
     lib.fd_plan_time_us.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), i32,
                                     i32]
     lib.fd_plan_time_us.restype = ctypes.c_double
@@ -221,6 +225,21 @@ def fd_plan_splits(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, 
     _check(lib.fd_plan_splits(batch, heads, kv_heads, dim, dtype, arr, num_cus, max_splits,
                               ctypes.byref(out)), "fd_plan_splits")
     return out.value
+
+
+def fd_plan_schedule(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, seqlens,
+                     num_cus: int = 0, max_splits: int = 0) -> tuple[int, int]:
+    """(schedule, num_splits) the library recommends for the batch: the
+    steal schedule with its layout where it measured faster, else the
+    static schedule with fd_plan_splits's count. Set the schedule with
+    fd_set_schedule before the call."""
+    lib = load_library()
+    lens = [int(x) for x in seqlens]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    sched, ns = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.fd_plan_schedule(batch, heads, kv_heads, dim, dtype, arr, num_cus, max_splits,
+                                ctypes.byref(sched), ctypes.byref(ns)), "fd_plan_schedule")
+    return sched.value, ns.value
 
 
 def fd_plan_time_us(batch: int, heads: int, kv_heads: int, dim: int, dtype: int, seqlens,

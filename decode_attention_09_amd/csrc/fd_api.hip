@@ -283,6 +283,16 @@ static_assert(kStealChunks >= 1 && kStealChunks <= fd::kStealMaxChunks,
               "the share word's front and back counts hold at most kStealMaxChunks");
 // Steal slots per share in the planner's layout for the steal schedule.
 constexpr int kStealPlanCap = 3;
+// fd_plan_schedule's rule for the steal schedule. Measured on MI355X, whole
+// calls in graph replay against the static schedule at the planner's split
+// count, Llama-3.1-8B shapes (bf16, 32/8 heads): every share streaming
+// 16.8-67 MB with lengths within 2x gains 1-8 % (B16 x 64K, 128K, 256K;
+// B8 x 256K; B4 x 512K; B2 x 1M; B16 x 64K-128K ragged), B32 x 64K (one
+// share per unit) is level, lengths within 3.7x gain 0.9 %; shares of
+// 8.4 MB (B16 x 32K) lose 1-3 %, of 2 MB (B1 x 128K) 7 %, and ragged
+// Qwen-shaped batches of 1-1.6 GB lose 0-10 %.
+constexpr int64_t kStealPlanMaxRatio = 4;
+constexpr double kStealPlanMinShareBytes = 12e6;
 
 // Shares per unit of a steal-scheduled call: the largest divisor d of
 // num_splits with at most one workgroup per compute unit (units * d <= cus)
@@ -538,6 +548,49 @@ int plan_inputs(int batch, int heads, int kv_heads, int dim, int dtype,
   return FD_OK;
 }
 
+// The static plan: among split counts that leave every split non-empty,
+// keep >= kPlanMinKeysPerSplit keys per split of the longest sequence and
+// a bounded workgroup count, the least modelled time; ties to fewer
+// splits. Launches of fewer workgroups than compute units are priced by
+// the same rounds (one round), which is the wave quantisation of
+// 04_flash_decoding.py demo 4 against the device's compute units.
+int plan_static_splits(const PlanInputs& p, int max_splits) {
+  int64_t cap = (p.max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
+  if (cap > p.min_len) cap = p.min_len;
+  if (cap > max_splits) cap = max_splits;
+  while (cap > 1 && p.units * cap > kMaxWorkgroups) --cap;
+  if (cap < 1) cap = 1;
+  double best = 0.0;
+  int choice = 1;
+  for (int64_t ns = 1; ns <= cap; ++ns) {
+    const double t = model_call_us(p.units, ns, p.cus, p.key_bytes, p.max_len, p.all_bytes,
+                                   p.min_len == p.max_len, p.partial_bytes_per_split * ns);
+    if (ns == 1 || t < best) {
+      best = t;
+      choice = (int)ns;
+    }
+  }
+  return choice;
+}
+
+// The steal layout's partial-slot count for a planned batch: as many
+// shares per unit as fit one per compute unit, each with kStealPlanCap
+// steal slots; 0 where the steal schedule cannot run (not the matrix-core
+// kernel, head dim other than 128), the slots exceed max_splits or the
+// words, or a share of the longest sequence would have fewer than two
+// chunks.
+int steal_plan_slots(const PlanInputs& p, int dim, int dtype, int max_splits) {
+  const bool mfma = g_path == FD_PATH_MFMA ||
+                    (g_path == FD_PATH_AUTO && auto_mfma(dtype, dim, p.sz.group));
+  if (!mfma || dim != 128) return 0;
+  const int64_t nsh = p.units < p.cus ? p.cus / p.units : 1;
+  const int64_t slots = nsh * (1 + kStealPlanCap);
+  if (slots > max_splits || p.units * nsh > fd::kStealMaxShares ||
+      p.max_len / nsh < 2 * fd::kStealMinChunk)
+    return 0;
+  return (int)slots;
+}
+
 }  // namespace
 
 extern "C" {
@@ -566,41 +619,37 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
   const int st = plan_inputs(batch, heads, kv_heads, dim, dtype, seqlens_host, num_cus, &p);
   if (st != FD_OK) return st;
   if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
-  // candidates: every split non-empty, the longest sequence keeps
-  // >= kPlanMinKeysPerSplit keys per split, workgroup count bounded
-  int64_t cap = (p.max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
-  if (cap > p.min_len) cap = p.min_len;
-  if (cap > max_splits) cap = max_splits;
-  while (cap > 1 && p.units * cap > kMaxWorkgroups) --cap;
-  if (cap < 1) cap = 1;
-  // the least modelled time; ties to fewer splits. Launches of fewer
-  // workgroups than compute units are priced by the same rounds (one round),
-  // which is the wave quantisation of 04_flash_decoding.py demo 4 against
-  // the device's compute units.
-  double best = 0.0;
-  int choice = 1;
-  for (int64_t ns = 1; ns <= cap; ++ns) {
-    const double t = model_call_us(p.units, ns, p.cus, p.key_bytes, p.max_len, p.all_bytes,
-                                   p.min_len == p.max_len, p.partial_bytes_per_split * ns);
-    if (ns == 1 || t < best) {
-      best = t;
-      choice = (int)ns;
+  // Under the steal schedule, a call that can take it gets the steal
+  // layout (steal_plan_slots); otherwise the least modelled time.
+  const int slots = g_sched == FD_SCHED_STEAL ? steal_plan_slots(p, dim, dtype, max_splits) : 0;
+  *num_splits_out = slots > 0 ? slots : plan_static_splits(p, max_splits);
+  return FD_OK;
+}
+
+int fd_plan_schedule(int batch, int heads, int kv_heads, int dim, int dtype,
+                     const int32_t* seqlens_host, int num_cus, int max_splits,
+                     int* schedule_out, int* num_splits_out) {
+  if (schedule_out == nullptr || num_splits_out == nullptr) return FD_ERR_INVALID_ARG;
+  PlanInputs p;
+  const int st = plan_inputs(batch, heads, kv_heads, dim, dtype, seqlens_host, num_cus, &p);
+  if (st != FD_OK) return st;
+  if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
+  // The steal schedule where it measured faster: a layout exists, the
+  // lengths lie within a factor of kStealPlanMaxRatio of each other, and
+  // each share of the longest sequence streams kStealPlanMinShareBytes or
+  // more (one K and one V row of one KV head per key).
+  const int slots = steal_plan_slots(p, dim, dtype, max_splits);
+  if (slots > 0) {
+    const int64_t nsh = slots / (1 + kStealPlanCap);
+    const double share_bytes = (double)(p.max_len / nsh) * p.key_bytes;
+    if (p.max_len <= kStealPlanMaxRatio * p.min_len && share_bytes >= kStealPlanMinShareBytes) {
+      *schedule_out = FD_SCHED_STEAL;
+      *num_splits_out = slots;
+      return FD_OK;
     }
   }
-  // Under the steal schedule, a call that can take it (matrix-core kernel,
-  // head dim 128) and whose longest sequence gives every share two chunks
-  // or more gets the steal layout instead: as many shares per unit as fit
-  // one per compute unit, each with kStealPlanCap steal slots.
-  const bool mfma = g_path == FD_PATH_MFMA ||
-                    (g_path == FD_PATH_AUTO && auto_mfma(dtype, dim, p.sz.group));
-  if (g_sched == FD_SCHED_STEAL && mfma && dim == 128) {
-    int64_t nsh = p.units < p.cus ? p.cus / p.units : 1;
-    const int64_t slots = nsh * (1 + kStealPlanCap);
-    if (slots <= max_splits && p.units * nsh <= fd::kStealMaxShares &&
-        p.max_len / nsh >= 2 * fd::kStealMinChunk)
-      choice = (int)slots;
-  }
-  *num_splits_out = choice;
+  *schedule_out = FD_SCHED_STATIC;
+  *num_splits_out = plan_static_splits(p, max_splits);
   return FD_OK;
 }
 

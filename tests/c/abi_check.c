@@ -18,6 +18,12 @@ int main(void) {
   st = fd_plan_splits(2, 8, 1, 128, FD_F16, empty, 256, 0, &ns);
   printf("plan_empty %d\n", st);
 
+  int32_t longs[16];
+  for (int i = 0; i < 16; ++i) longs[i] = 131072;
+  int planned = -1;
+  st = fd_plan_schedule(16, 32, 8, 128, FD_BF16, longs, 256, 0, &planned, &ns);
+  printf("plan_sched %d %d %d\n", st, planned, ns);
+
   printf("ws %zu\n", fd_workspace_bytes(2, 8, 4, 128));
   /* argument order (batch, heads, num_splits, dim): 128 splits of dim 64
    * and 64 splits of dim 128 need different sizes, so a swap shows */

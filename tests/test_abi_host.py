@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_attention", "fd_decode_split",
               "fd_decode_combine", "fd_status_string", "fd_last_error", "fd_set_kernel_path",
               "fd_workspace_bytes_unnorm", "fd_decode_split_unnorm", "fd_decode_combine_unnorm",
-              "fd_decode_attention_unnorm", "fd_set_schedule", "fd_decode_attention_noalloc", "fd_set_combine"):
+              "fd_decode_attention_unnorm", "fd_set_schedule", "fd_decode_attention_noalloc", "fd_set_combine",
+              "fd_plan_schedule", "fd_plan_time_us"):
         assert n in names
 
 
@@ -416,3 +417,32 @@ def test_planner_gives_the_steal_layout_under_the_steal_schedule():
     finally:
         fd.fd_set_schedule(prev)
     assert valu_steal == plan(16, 32, 8, 128, [131072] * 16, dtype=fd.FD_BF16) != 8
+
+
+def test_plan_schedule_recommends_steal_for_long_even_shares():
+    # the steal schedule where it measured faster on MI355X: matrix-core
+    # kernel (head dim 128), lengths within 4x, shares of >= 12 MB of K+V
+    def ps(B, H, Hkv, D, lens, dtype=fd.FD_BF16, cus=256):
+        return fd.fd_plan_schedule(B, H, Hkv, D, dtype, lens, cus, 0)
+    steal, static = fd.FD_SCHED_STEAL, fd.FD_SCHED_STATIC
+    assert ps(16, 32, 8, 128, [131072] * 16) == (steal, 8)      # 32 MB shares
+    assert ps(16, 32, 8, 128, [65536] * 16) == (steal, 8)       # 16.8 MB
+    assert ps(2, 32, 8, 128, [1 << 20] * 2) == (steal, 64)      # 16 units: 16 shares each
+    assert ps(16, 32, 8, 128, [131072] * 8 + [32768] * 8) == (steal, 8)   # within 4x
+    # shorter shares, ragged batches, other kernels: the static plan
+    for args, kw in (((16, 32, 8, 128, [32768] * 16), {}),            # 8.4 MB shares
+                     ((1, 32, 8, 128, [131072]), {}),                 # 2 MB shares
+                     ((16, 32, 8, 128, [131072] * 8 + [30000] * 8), {}),  # 4.4x apart
+                     ((16, 32, 8, 64, [131072] * 16), {}),            # head dim 64
+                     ((16, 32, 32, 128, [131072] * 16), {}),          # MHA: VALU kernel
+                     ((32, 28, 4, 128, [32768] * 32), {"dtype": fd.FD_F16})):
+        sched, ns = ps(*args, **kw)
+        assert sched == static, args
+        assert ns == fd.fd_plan_splits(*args[:4], kw.get("dtype", fd.FD_BF16), args[4], 256, 0)
+    prev = fd.fd_set_kernel_path(fd.FD_PATH_VALU)
+    try:
+        assert ps(16, 32, 8, 128, [131072] * 16)[0] == static
+    finally:
+        fd.fd_set_kernel_path(prev)
+    with pytest.raises(fd.FdError):
+        ps(2, 32, 8, 128, [5, 0])

@@ -38,6 +38,7 @@ def test_c_program(c_program):
     st, ns = out["plan"].split()
     assert st == "0" and 1 <= int(ns) <= 16
     assert out["plan_empty"] == "3"
+    assert out["plan_sched"] == "0 3 8"   # FD_OK, FD_SCHED_STEAL, 8 slots
     rows = 2 * 8 * 4
     # control block: claim counter 256 B, arrival counters padded to 256 B,
     # 4096 share words of the steal schedule
