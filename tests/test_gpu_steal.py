@@ -177,6 +177,8 @@ CASES = [  # (name, workload, lengths or None, num_splits)
     ("prime_ns7", W.Workload("p7", 2, 8, 2, 128, "f16", kv_len=None), [12000, 3001], 7),
     ("bhsd", W.Workload("bhsd", 3, 16, 4, 128, "bf16", kv_len=None, layout="bhsd"),
      [7000, 2500, 9000], 8),
+    # 32 units, 128 slots: 8 shares per unit with the largest steal count, 15
+    ("cap15", W.llama(4, 40000), None, 128),
 ]
 
 
@@ -347,6 +349,7 @@ def test_share_layout_rule():
     if cus == 256:
         assert shares_per_unit(128, 8, cus) == 2
         assert shares_per_unit(8, 128, cus) == 32
+        assert shares_per_unit(32, 128, cus) == 8     # 15 steal slots per share
 
 
 def test_schedule_is_per_thread():
