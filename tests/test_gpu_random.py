@@ -44,7 +44,7 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 120
+N_CASES = 200
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "unpacked": 3}
 def _draw(i: int):
     rng = np.random.default_rng(20261202 + i)
