@@ -90,6 +90,18 @@ int main(void) {
     calls += 3;
     CHECK(w1 > 0 && w2 >= w1 && u1 > 0, "workspace %zu %zu %zu", w1, w2, u1);
     CHECK(w1 >= (size_t)batch * heads * ns * ((size_t)dim + 1) * 4, "workspace too small");
+
+    /* the recommended schedule: a known schedule and a split count within
+       bounds; the static recommendation is fd_plan_splits's own count */
+    int sched = -1, ns2 = -7;
+    const int st2 = fd_plan_schedule(batch, heads, kv_heads, dim, dtype, lens, cus, cap, &sched,
+                                     &ns2);
+    ++calls;
+    CHECK(st2 == FD_OK, "plan_schedule st %d", st2);
+    CHECK(sched == FD_SCHED_STATIC || sched == FD_SCHED_STEAL, "schedule %d", sched);
+    CHECK(ns2 >= 1 && ns2 <= limit, "plan_schedule ns %d outside [1, %d]", ns2, limit);
+    if (sched == FD_SCHED_STATIC) CHECK(ns2 == ns, "static ns %d vs %d", ns2, ns);
+    if (sched == FD_SCHED_STEAL) CHECK(dim == 128 && ns2 % 4 == 0, "steal ns %d dim %d", ns2, dim);
   }
 
   /* argument edges */
@@ -101,6 +113,15 @@ int main(void) {
   CHECK(fd_plan_splits(1, 8, 1, 128, 7, lens, 256, 0, &ns) == FD_ERR_UNSUPPORTED, "dtype 7");
   CHECK(fd_plan_splits(1, 8, 1, 128, FD_F16, NULL, 256, 0, &ns) == FD_ERR_INVALID_ARG, "null");
   CHECK(fd_plan_splits(1, 8, 1, 128, FD_F16, lens, -1, 0, &ns) == FD_ERR_INVALID_ARG, "cus -1");
+  {
+    int sched = 0;
+    CHECK(fd_plan_schedule(1, 8, 1, 128, FD_F16, lens, 256, 0, NULL, &ns) == FD_ERR_INVALID_ARG,
+          "null schedule");
+    CHECK(fd_plan_schedule(1, 8, 1, 128, FD_F16, lens, 256, 0, &sched, NULL) == FD_ERR_INVALID_ARG,
+          "null count");
+    CHECK(fd_plan_schedule(1, 8, 1, 128, FD_F16, NULL, 256, 0, &sched, &ns) == FD_ERR_INVALID_ARG,
+          "null lengths");
+  }
   CHECK(fd_workspace_bytes(INT32_MAX, INT32_MAX, FD_MAX_SPLITS, 128) == 0, "overflow size");
   CHECK(fd_workspace_bytes(1, 1, FD_MAX_SPLITS + 1, 128) == 0, "too many splits");
   CHECK(fd_workspace_bytes_unnorm(1, 1, 2, 100) == 0, "bad dim");
