@@ -421,3 +421,18 @@ def test_noalloc_entry_point_under_the_steal_schedule():
             check_vs_oracle(inp, out)
     finally:
         fd.fd_set_schedule(prev)
+
+
+def test_garbage_in_the_control_block():
+    """The reset kernel zeroes the share words before each steal launch:
+    a workspace whose partials, arrival counters and share words all hold
+    0x7f bytes gives the oracle's output and clean word invariants."""
+    fd = H.fd()
+    w = W.llama(16, 8192)
+    inp = W.make_inputs(w, H.DEV, seed=12)
+    ns = 8
+    ws = torch.full((fd.fd_workspace_bytes(w.batch, w.heads, ns, w.dim),), 0x7f,
+                    dtype=torch.uint8, device=H.DEV)
+    out, ws = steal_call(inp, ns, workspace=ws)
+    check_vs_oracle(inp, out)
+    check_workspace(inp, ns, ws)
