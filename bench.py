@@ -75,29 +75,27 @@ def workload_by_name(name: str):
                      + ", ".join(w.name for w in W.all_workloads()))
 
 
-# Schedule for workloads whose split count the pages fix, where the
-# library's planner does not choose: the queue schedule on the ragged varlen
-# batch at its 8 splits (the header's advice for ragged batches; A/B in one
-# process on MI355X, whole calls in graph replay: 201.9 -> 187.2 us).
-BENCH_SCHEDULE = {"varlen_qwen7b_b32_h28kv4_d128_f16": "queue"}
-
-
-def set_schedule(fd, w, requested, ns_override=0):
+def choose_schedule(fd, w, requested, lengths, ns_override=0):
     """Set the calling thread's schedule for workload w before its split
-    count is planned: the requested one, else BENCH_SCHEDULE's, else, where
-    the planner picks the split count, fd_plan_schedule's recommendation,
-    else the library's default. Returns its name."""
+    count is planned: the requested one, else fd_plan_schedule's
+    recommendation for these lengths -- taken with its split count where
+    the planner sets the count, and where the workload fixes the count only
+    if the recommendation's count is the same. Returns (schedule name,
+    split count or 0 for the planner's)."""
     code = {"auto": fd.FD_SCHED_AUTO, "static": fd.FD_SCHED_STATIC,
             "queue": fd.FD_SCHED_QUEUE, "steal": fd.FD_SCHED_STEAL}
-    name = requested or BENCH_SCHEDULE.get(w.name)
-    if name is None and w.num_splits is None and not ns_override and w.kv_len is not None:
-        lengths = [w.kv_len] * w.batch
+    names = {v: k for k, v in code.items()}
+    name, planned = requested or "auto", 0
+    if requested is None and min(lengths) > 0:
         dt = {"f32": fd.FD_F32, "f16": fd.FD_F16, "bf16": fd.FD_BF16}[w.dtype]
-        sched, _ = fd.fd_plan_schedule(w.batch, w.heads, w.kv_heads, w.dim, dt, lengths)
-        name = {v: k for k, v in code.items()}[sched]
-    name = name or "auto"
+        rec, ns_rec = fd.fd_plan_schedule(w.batch, w.heads, w.kv_heads, w.dim, dt, lengths)
+        fixed = pick_splits(w, lengths, ns_override) if (ns_override or w.num_splits) else 0
+        if not fixed:
+            name, planned = names[rec], ns_rec
+        elif fixed == ns_rec:
+            name = names[rec]
     fd.fd_set_schedule(code[name])
-    return name
+    return name, planned
 
 
 def pick_splits(w, lengths, override=0):
@@ -198,7 +196,7 @@ def split_workgroups(w, ns: int, rows_per_workgroup: int, schedule: str = "auto"
 
 def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LLC_BYTES,
         ns_override: int = 0, rows_per_workgroup: int = 8, fmt: str = "lse", graph: bool = False,
-        schedule: str = "auto"):
+        schedule: str | None = None):
     import torch
     import workloads as W
     import decode_attention_09_amd as fd
@@ -206,7 +204,8 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = W.make_inputs(w, dev, seed=0)
-    ns = pick_splits(w, inp.lengths, ns_override)
+    schedule, planned = choose_schedule(fd, w, schedule, inp.lengths, ns_override)
+    ns = planned or pick_splits(w, inp.lengths, ns_override)
     kv_bytes = inp.kv_bytes
     copies = max(1, min(16, math.ceil(copies_min_bytes / max(1, kv_bytes))))
     ks = [inp.k] + [inp.k.clone() for _ in range(copies - 1)]
@@ -303,6 +302,7 @@ def run(w, steps: int, warmup: int, cpu_s: float, copies_min_bytes: int = 3 * LL
         "per_call_us": {"p10": pct(0.10), "p50": pct(0.50), "p90": pct(0.90), "calls": steps,
                         "how": "HIP events around each call"},
         "higher_is_better": True,
+        "schedule": schedule,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
@@ -385,7 +385,7 @@ def fit_planner(steps: int, warmup: int):
     for name, splits in FIT_SWEEPS:
         w = workload_by_name(name)
         for ns in splits:
-            r = run(w, steps, warmup, 0.0, ns_override=ns, graph=True)
+            r = run(w, steps, warmup, 0.0, ns_override=ns, graph=True, schedule="static")
             G = w.group
             pts.append(dict(workload=name, ns=ns, batch=w.batch, heads=w.heads,
                             kv_heads=w.kv_heads, dim=w.dim, kv_len=w.kv_len,
@@ -455,8 +455,8 @@ def main():
                          "unpacked = one query head per workgroup, the comparison path)")
     ap.add_argument("--schedule", choices=["auto", "static", "queue", "steal"], default=None,
                     help="how split launches hand segments to workgroups (default: "
-                         "BENCH_SCHEDULE's entry for the workload, else the library's "
-                         "choice; queue = a device-sized grid claiming segments from a "
+                         "fd_plan_schedule's recommendation for the workload's lengths; "
+                         "queue = a device-sized grid claiming segments from a "
                          "counter; steal = one workgroup per share of each unit, chunks "
                          "claimed ahead, idle workgroups taking the back half of another "
                          "share's unclaimed chunks)")
@@ -505,22 +505,18 @@ def main():
                     for ns in splits]
         cpu_s = args.cpu_seconds or 0.0
         for w, ns in todo:
-            sched = set_schedule(fd, w, args.schedule, ns)
             r = run(w, args.steps, args.warmup, cpu_s, ns_override=ns, rows_per_workgroup=rows,
-                    fmt=args.format, graph=args.graph, schedule=sched)
+                    fmt=args.format, graph=args.graph, schedule=args.schedule)
             r["kernel_path"] = args.kernel_path
-            r["schedule"] = sched
             r["combine"] = args.combine
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
         return
     cpu_s = 10.0 if args.cpu_seconds is None else args.cpu_seconds
     w = workload_by_name(args.workload)
-    sched = set_schedule(fd, w, args.schedule, args.num_splits)
     r = run(w, args.steps, args.warmup, cpu_s, ns_override=args.num_splits,
-            rows_per_workgroup=rows, fmt=args.format, graph=args.graph, schedule=sched)
+            rows_per_workgroup=rows, fmt=args.format, graph=args.graph, schedule=args.schedule)
     r["kernel_path"] = args.kernel_path
-    r["schedule"] = sched
     r["combine"] = args.combine
     print(json.dumps(r), flush=True)
 

@@ -293,6 +293,16 @@ constexpr int kStealPlanCap = 3;
 // Qwen-shaped batches of 1-1.6 GB lose 0-10 %.
 constexpr int64_t kStealPlanMaxRatio = 4;
 constexpr double kStealPlanMinShareBytes = 12e6;
+// fd_plan_schedule's rule for ragged batches (longest >= 1.5x shortest):
+// the queue schedule with about this many segments per compute unit.
+// Measured on MI355X, whole calls in graph replay: on every ragged batch
+// tried (Qwen-shaped B32 with lengths 1K-32K, 8K-32K, 16K-32K and 64-32K;
+// Llama-shaped B16 with 32K-128K and 64K-128K; B4 with 8K-64K) the queue at
+// 4 segments per CU was the fastest option or within 1.3 % of it (e.g.
+// Qwen 1K-32K: 161 us against 169-180 static at 12-28 splits and 168-188
+// queued at 12-28; Llama 32K-128K: 728-752 us against 767-806 static); at
+// 2 per CU it lost 9 % (Qwen 1K-32K), at 8 per CU -1 to +7 %.
+constexpr int64_t kQueuePlanSegmentsPerCu = 4;
 
 // Shares per unit of a steal-scheduled call: the largest divisor d of
 // num_splits with at most one workgroup per compute unit (units * d <= cus)
@@ -634,10 +644,29 @@ int fd_plan_schedule(int batch, int heads, int kv_heads, int dim, int dtype,
   const int st = plan_inputs(batch, heads, kv_heads, dim, dtype, seqlens_host, num_cus, &p);
   if (st != FD_OK) return st;
   if (max_splits <= 0 || max_splits > FD_MAX_SPLITS) max_splits = FD_MAX_SPLITS;
-  // The steal schedule where it measured faster: a layout exists, the
-  // lengths lie within a factor of kStealPlanMaxRatio of each other, and
-  // each share of the longest sequence streams kStealPlanMinShareBytes or
-  // more (one K and one V row of one KV head per key).
+  // Ragged batches: the queue schedule at about kQueuePlanSegmentsPerCu
+  // segments per compute unit (never more splits than the shortest
+  // sequence has keys, nor fewer than 256 keys per split of the longest).
+  if (2 * p.max_len >= 3 * p.min_len) {
+    int64_t ns = (kQueuePlanSegmentsPerCu * (int64_t)p.cus + p.units / 2) / p.units;
+    const int64_t keys_cap = (p.max_len + kPlanMinKeysPerSplit - 1) / kPlanMinKeysPerSplit;
+    if (ns > keys_cap) ns = keys_cap;
+    if (ns > p.min_len) ns = p.min_len;
+    if (ns > max_splits) ns = max_splits;
+    while (ns > 1 && p.units * ns > kMaxWorkgroups) --ns;
+    if (ns < 1) ns = 1;
+    // the queue runs only where the launch fills the device
+    if (p.units * ns >= p.cus) {
+      *schedule_out = FD_SCHED_QUEUE;
+      *num_splits_out = (int)ns;
+      return FD_OK;
+    }
+  }
+  // Near-uniform batches: the steal schedule where it measured faster: a
+  // layout exists, the lengths lie within a factor of kStealPlanMaxRatio of
+  // each other, and each share of the longest sequence streams
+  // kStealPlanMinShareBytes or more (one K and one V row of one KV head per
+  // key).
   const int slots = steal_plan_slots(p, dim, dtype, max_splits);
   if (slots > 0) {
     const int64_t nsh = slots / (1 + kStealPlanCap);

@@ -132,15 +132,20 @@ int fd_plan_splits(int batch, int heads, int kv_heads, int dim, int dtype,
 /*
  * fd_plan_schedule -- the schedule (fd_set_schedule) and split count the
  * library recommends for a batch (host only, arguments as fd_plan_splits).
- * *schedule_out = FD_SCHED_STEAL with the steal layout's slot count (see
- * fd_plan_splits) when the call would run the matrix-core kernel at head
- * dim 128, the longest sequence is at most 4x the shortest, and each share
- * of the longest sequence streams >= 12 MB of K and V; otherwise
- * FD_SCHED_STATIC with fd_plan_splits's count under the static schedule.
- * The rule is MI355X's measured one (Llama-3.1-8B-shaped calls of 4-17 GB
- * with such shares run 1-8 % faster under the steal schedule, shorter
- * shares and ragged batches slower). The caller sets the schedule with
- * fd_set_schedule before the call. Errors as fd_plan_splits.
+ * Ragged batches (longest sequence >= 1.5x the shortest): FD_SCHED_QUEUE
+ * with about 4 segments per compute unit, num_splits = round(4 * num_cus /
+ * units) (units = batch * kv_heads * ceil(group / 8)), capped by the
+ * shortest sequence, 256 keys per split of the longest and max_splits,
+ * where that fills the device. Otherwise FD_SCHED_STEAL with the steal
+ * layout's slot count (see fd_plan_splits) when the call would run the
+ * matrix-core kernel at head dim 128, the longest sequence is at most 4x
+ * the shortest and each share of the longest sequence streams >= 12 MB of
+ * K and V; else FD_SCHED_STATIC with fd_plan_splits's count. The rules are
+ * MI355X's measured ones (the queue at 4 segments per CU was the fastest
+ * option or within 1.3 % of it on every ragged batch tried; near-uniform
+ * Llama-3.1-8B-shaped calls of 4-17 GB with such shares run 1-8 % faster
+ * under the steal schedule, shorter shares slower). The caller sets the
+ * schedule with fd_set_schedule before the call. Errors as fd_plan_splits.
  */
 int fd_plan_schedule(int batch, int heads, int kv_heads, int dim, int dtype,
                      const int32_t* seqlens_host, int num_cus, int max_splits,

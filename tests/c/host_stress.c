@@ -98,8 +98,10 @@ int main(void) {
                                      &ns2);
     ++calls;
     CHECK(st2 == FD_OK, "plan_schedule st %d", st2);
-    CHECK(sched == FD_SCHED_STATIC || sched == FD_SCHED_STEAL, "schedule %d", sched);
+    CHECK(sched == FD_SCHED_STATIC || sched == FD_SCHED_STEAL || sched == FD_SCHED_QUEUE,
+          "schedule %d", sched);
     CHECK(ns2 >= 1 && ns2 <= limit, "plan_schedule ns %d outside [1, %d]", ns2, limit);
+    if (sched == FD_SCHED_QUEUE) CHECK(ns2 <= min_len, "queue ns %d > shortest %d", ns2, (int)min_len);
     if (sched == FD_SCHED_STATIC) CHECK(ns2 == ns, "static ns %d vs %d", ns2, ns);
     if (sched == FD_SCHED_STEAL) CHECK(dim == 128 && ns2 % 4 == 0, "steal ns %d dim %d", ns2, dim);
   }

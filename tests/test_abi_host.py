@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -420,19 +421,19 @@ def test_planner_gives_the_steal_layout_under_the_steal_schedule():
 
 
 def test_plan_schedule_recommends_steal_for_long_even_shares():
-    # the steal schedule where it measured faster on MI355X: matrix-core
-    # kernel (head dim 128), lengths within 4x, shares of >= 12 MB of K+V
+    # near-uniform batches: the steal schedule where it measured faster on
+    # MI355X: matrix-core kernel (head dim 128), lengths within 1.5x, shares
+    # of >= 12 MB of K+V
     def ps(B, H, Hkv, D, lens, dtype=fd.FD_BF16, cus=256):
         return fd.fd_plan_schedule(B, H, Hkv, D, dtype, lens, cus, 0)
     steal, static = fd.FD_SCHED_STEAL, fd.FD_SCHED_STATIC
     assert ps(16, 32, 8, 128, [131072] * 16) == (steal, 8)      # 32 MB shares
     assert ps(16, 32, 8, 128, [65536] * 16) == (steal, 8)       # 16.8 MB
     assert ps(2, 32, 8, 128, [1 << 20] * 2) == (steal, 64)      # 16 units: 16 shares each
-    assert ps(16, 32, 8, 128, [131072] * 8 + [32768] * 8) == (steal, 8)   # within 4x
-    # shorter shares, ragged batches, other kernels: the static plan
+    assert ps(16, 32, 8, 128, [131072] * 8 + [98304] * 8) == (steal, 8)   # within 1.5x
+    # shorter shares, other kernels: the static plan
     for args, kw in (((16, 32, 8, 128, [32768] * 16), {}),            # 8.4 MB shares
                      ((1, 32, 8, 128, [131072]), {}),                 # 2 MB shares
-                     ((16, 32, 8, 128, [131072] * 8 + [30000] * 8), {}),  # 4.4x apart
                      ((16, 32, 8, 64, [131072] * 16), {}),            # head dim 64
                      ((16, 32, 32, 128, [131072] * 16), {}),          # MHA: VALU kernel
                      ((32, 28, 4, 128, [32768] * 32), {"dtype": fd.FD_F16})):
@@ -446,3 +447,24 @@ def test_plan_schedule_recommends_steal_for_long_even_shares():
         fd.fd_set_kernel_path(prev)
     with pytest.raises(fd.FdError):
         ps(2, 32, 8, 128, [5, 0])
+
+
+def test_plan_schedule_recommends_the_queue_for_ragged_batches():
+    # longest >= 1.5x shortest: the queue schedule at ~4 segments per CU,
+    # round(4 * cus / units) splits, capped by the shortest sequence and
+    # 256 keys per split of the longest, where the launch fills the device
+    def ps(B, H, Hkv, D, lens, dtype=fd.FD_F16, cus=256):
+        return fd.fd_plan_schedule(B, H, Hkv, D, dtype, lens, cus, 0)
+    queue, static = fd.FD_SCHED_QUEUE, fd.FD_SCHED_STATIC
+    rng = np.random.default_rng(5)
+    varlen = [int(x) for x in rng.integers(64, 32769, size=32)]
+    assert ps(32, 28, 4, 128, varlen) == (queue, 8)                         # 128 units
+    assert ps(16, 32, 8, 128, [131072] * 8 + [32768] * 8, fd.FD_BF16) == (queue, 8)
+    assert ps(4, 32, 8, 128, [8192, 65536, 20000, 40000], fd.FD_BF16) == (queue, 32)
+    assert ps(32, 28, 4, 64, varlen) == (queue, 8)        # any head dim and kernel
+    assert ps(32, 28, 4, 128, varlen, cus=80) == (queue, 3)   # round(320 / 128)
+    # capped by the shortest sequence
+    assert ps(32, 28, 4, 128, [5] + [30000] * 31) == (queue, 5)
+    # a ragged launch that cannot fill the device: not the queue
+    sched, ns = ps(2, 8, 1, 128, [3000, 1000])
+    assert sched != queue
