@@ -46,6 +46,17 @@ DEFAULT_WORKLOAD = "llama8b_b16_l131072_h32kv8_d128_bf16"
 PEAK_GBS = 8000.0
 LLC_BYTES = 256 * 2 ** 20       # MI355X Infinity Cache (MALL)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Workloads measured briefly beside the headline in a default run: the other
+# long-context and GQA points (flash-decoding 16/2-head shapes, Llama-8B at
+# batch 1 and 16, the varlen Qwen batch) and the MHA D = 128 shape.
+CONTEXT_WORKLOADS = [
+    "fd_ubench_b8_l8192_h16kv2_d128_f16",
+    "fd_ubench_b1_l65536_h16kv2_d128_f16",
+    "llama8b_b1_l131072_h32kv8_d128_bf16",
+    "llama8b_b16_l32768_h32kv8_d128_bf16",
+    "varlen_qwen7b_b32_h28kv4_d128_f16",
+    "mha_b4_h32_l4096_d128_f16",
+]
 KERNEL_SOURCES = ["fd_split.h", "fd_internal.h", "fd_steal.h"]
 
 
@@ -418,6 +429,27 @@ def fit_planner(steps: int, warmup: int):
                       "max_rel": round(max(rel), 4), "cus": cus, "points": pts}), flush=True)
 
 
+def context_points(names, steps: int = 100, warmup: int = 100):
+    """Short runs of other workloads after the headline, each replayed from
+    a captured HIP graph (so the host's per-call issue cost, which bounds
+    the smallest shapes when calls are issued one by one, stays out): whole
+    call and split kernel, each as a fraction of 8 TB/s on its K/V bytes."""
+    import torch
+    pts = []
+    for n in names:
+        torch.cuda.empty_cache()
+        r = run(workload_by_name(n), steps, warmup, 0.0, graph=True)
+        pts.append({"workload": n, "schedule": r["schedule"],
+                    "num_splits": r["config"]["num_splits"],
+                    "kv_bytes": r["config"]["kv_bytes"],
+                    "us_per_call": r["us_per_call"],
+                    "call_frac": round(r["value"] / PEAK_GBS, 4),
+                    "split_kernel_us": r["roofline"]["kernel_us"],
+                    "split_frac": r["roofline"]["frac"],
+                    "traffic": r["roofline"]["traffic"]})
+    return {"timing": f"graph replay, {steps} calls after {warmup}", "points": pts}
+
+
 def copy_calibration(mib: int):
     """Ten device-to-device copies of a mib-MiB buffer: a kernel that reads
     and writes exactly mib MiB per launch, to scale the HBM byte counters."""
@@ -441,7 +473,12 @@ def main():
     # calls at ~1285 us before ~1236 us), so the default warm-up spans
     # ~0.12 s of the bench line.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help=f"workload name (default {DEFAULT_WORKLOAD}; without this flag the "
+                         "line also carries short graph-replayed runs of the other long-context "
+                         "and GQA workloads under 'context')")
+    ap.add_argument("--no-context", action="store_true",
+                    help="leave out the 'context' runs of a default invocation")
     ap.add_argument("--all", action="store_true",
                     help="one line per workload (no CPU leg unless --cpu-seconds is given)")
     ap.add_argument("--cpu-seconds", type=float, default=None,
@@ -501,7 +538,8 @@ def main():
             todo = [(w, args.num_splits) for w in W.all_workloads()]
         else:
             splits = [int(x) for x in args.sweep_splits.split(",") if x]
-            todo = [(workload_by_name(n), ns) for n in args.workload.split(",")
+            todo = [(workload_by_name(n), ns)
+                    for n in (args.workload or DEFAULT_WORKLOAD).split(",")
                     for ns in splits]
         cpu_s = args.cpu_seconds or 0.0
         for w, ns in todo:
@@ -513,11 +551,14 @@ def main():
             torch.cuda.empty_cache()
         return
     cpu_s = 10.0 if args.cpu_seconds is None else args.cpu_seconds
-    w = workload_by_name(args.workload)
+    w = workload_by_name(args.workload or DEFAULT_WORKLOAD)
     r = run(w, args.steps, args.warmup, cpu_s, ns_override=args.num_splits,
             rows_per_workgroup=rows, fmt=args.format, graph=args.graph, schedule=args.schedule)
     r["kernel_path"] = args.kernel_path
     r["combine"] = args.combine
+    if args.workload is None and not args.no_context and not args.num_splits \
+            and args.schedule is None and args.format == "lse":
+        r["context"] = context_points(CONTEXT_WORKLOADS)
     print(json.dumps(r), flush=True)
 
 

@@ -79,3 +79,20 @@ def test_default_workload_is_the_largest_configuration():
     biggest = max(W.all_workloads(), key=kv_bytes)
     assert bench.DEFAULT_WORKLOAD == biggest.name == "llama8b_b16_l131072_h32kv8_d128_bf16"
     assert kv_bytes(biggest) == 16 * 131072 * 8 * 128 * 2 * 2
+
+
+def test_context_points_are_the_other_long_context_and_gqa_workloads():
+    """A default bench run also times these workloads briefly: each is a
+    known workload with a committed traffic entry, none is the headline,
+    and together they cover the flash-decoding 16/2-head shapes, Llama-8B
+    at batch 1 and 16, and the varlen batch."""
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    names = bench.CONTEXT_WORKLOADS
+    assert len(set(names)) == len(names) and bench.DEFAULT_WORKLOAD not in names
+    ws = [bench.workload_by_name(n) for n in names]
+    assert all(n in t for n in names)
+    assert any(w.heads == 16 and w.kv_heads == 2 for w in ws)
+    assert {w.batch for w in ws if w.name.startswith("llama8b")} == {1, 16}
+    assert any(w.varlen_range is not None for w in ws)
+
