@@ -197,6 +197,37 @@ def test_queue_schedule_is_bitwise_equal_to_static(case, kernel_path):
         assert H.max_err(H.host(q[0]), H.oracle_full(inp, ns)) <= H.TOL[w.dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_queue_schedule_with_empty_sequences_and_splits(dtype, kernel_path):
+    """Segments of no tile (empty sequences, more splits than keys) and of
+    fewer tiles than a workgroup has waves, claimed through the queue: the
+    claim of the next segment is then made after the walk. Output and
+    partials bitwise equal to the static schedule's."""
+    fd = H.fd()
+    lengths = [0, 5, 100, 0, 3000, 1, 64, 0, 17, 513, 2, 7000, 33, 0, 250, 16]
+    w = W.Workload("qempty", len(lengths), 8, 2, 128, dtype, kv_len=None)
+    inp = W.make_inputs(w, H.DEV, seed=6, lengths=lengths)
+    ns = 16
+    n = fd.fd_workspace_bytes(w.batch, w.heads, ns, w.dim)
+    _, ctl_off, _ = _layout_sizes(w, ns)
+    res = {}
+    for sched in (fd.FD_SCHED_STATIC, fd.FD_SCHED_QUEUE):
+        ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=H.DEV)
+        prev = fd.fd_set_schedule(sched)
+        try:
+            H.announce("schedule", sched, w.name, dtype, f"ns={ns}")
+            out = fd.fd_decode_attention(inp.q, inp.k, inp.v, inp.cu_seqlens_k, ns,
+                                         workspace=ws, layout=w.layout)
+            torch.cuda.synchronize()
+        finally:
+            fd.fd_set_schedule(prev)
+        res[sched] = (out, ws[:ctl_off].clone())
+    s, q = res[fd.FD_SCHED_STATIC], res[fd.FD_SCHED_QUEUE]
+    assert _bitwise(s[0], q[0]), "outputs differ"
+    assert _bitwise(s[1], q[1]), "partials differ"
+    assert torch.isfinite(q[0]).all()
+
+
 def test_queue_schedule_under_graph_replay():
     """The counter reset is a kernel node: every replay of a captured queued
     call starts from zero and equals the eager call."""
