@@ -438,7 +438,11 @@ def context_points(names, steps: int = 100, warmup: int = 100):
     pts = []
     for n in names:
         torch.cuda.empty_cache()
-        r = run(workload_by_name(n), steps, warmup, 0.0, graph=True)
+        try:
+            r = run(workload_by_name(n), steps, warmup, 0.0, graph=True)
+        except Exception as e:  # a context point never costs the headline its line
+            pts.append({"workload": n, "error": f"{type(e).__name__}: {e}"})
+            continue
         pts.append({"workload": n, "schedule": r["schedule"],
                     "num_splits": r["config"]["num_splits"],
                     "kv_bytes": r["config"]["kv_bytes"],
