@@ -424,6 +424,54 @@ def pin_states_sdpa(orc):
         assert m.shape == (B, H, ns) and l.shape == (B, H, ns) and acc.shape == (B, H, ns, D)
 
 
+# --------------------------------------------------------------------------
+# whole-batch split partials (the workspace's layout), against the library
+# --------------------------------------------------------------------------
+def pin_batch_partials(orc):
+    """attention_partials on varlen batches whose offsets do not start at 0,
+    in both layouts: partial s of head h of sequence b is torch float64 SDPA
+    over that sequence's keys [L*s/ns, L*(s+1)/ns) (the bounds of
+    decode_attention_splitkv.py), and its LSE, stored at [b, s, h], is
+    scipy's logsumexp of the scaled scores over the same keys."""
+    from scipy.special import logsumexp
+    rng = _rng(11)
+    for layout in ("packed", "bhsd"):
+        for (H, Hkv, D, lens, ns, off) in [(4, 2, 8, [9, 13, 7], 3, 3), (6, 3, 16, [20, 11], 5, 0),
+                                           (8, 1, 4, [6], 6, 2)]:
+            B, G = len(lens), H // Hkv
+            q = rng.standard_normal((B, H, D))
+            scale = 0.3
+            cu = [off]
+            for L in lens:
+                cu.append(cu[-1] + L)
+            if layout == "packed":
+                kv_k = rng.standard_normal((cu[-1] + 2, Hkv, D))
+                kv_v = rng.standard_normal((cu[-1] + 2, Hkv, D))
+                cu_arg = cu
+                rows = lambda kv, b, j: kv[cu[b]:cu[b + 1], j]
+            else:
+                S = max(lens) + 1
+                kv_k = rng.standard_normal((B, Hkv, S, D))
+                kv_v = rng.standard_normal((B, Hkv, S, D))
+                cu_arg = [0]
+                for L in lens:
+                    cu_arg.append(cu_arg[-1] + L)
+                rows = lambda kv, b, j: kv[b, j, :lens[b]]
+            op, lse = orc.attention_partials(q, kv_k, kv_v, cu_arg, H, Hkv, ns, scale,
+                                             layout=layout)
+            assert op.shape == (B, H, ns, D) and lse.shape == (B, ns, H)
+            for b, L in enumerate(lens):
+                for h in range(H):
+                    kr, vr = rows(kv_k, b, h // G), rows(kv_v, b, h // G)
+                    for s in range(ns):
+                        a, e = L * s // ns, L * (s + 1) // ns
+                        ref = _sdpa(q[b:b + 1, h:h + 1], kr[None, None, a:e], vr[None, None, a:e],
+                                    scale, 1)[0, 0]
+                        assert np.abs(op[b, h, s] - ref).max() < 1e-12, (layout, b, h, s)
+                        ref_lse = logsumexp(scale * (kr[a:e] @ q[b, h]))
+                        assert abs(lse[b, s, h] - ref_lse) < 1e-12, (layout, b, h, s)
+
+
 ALL_PINS = [pin_split_bounds, pin_closed_forms, pin_decimal_bruteforce, pin_torch_sdpa,
             pin_split_invariant, pin_metamorphic, pin_split_bounds_ceil, pin_states_decimal,
-            pin_states_closed_forms, pin_states_sdpa]
+            pin_states_closed_forms, pin_states_sdpa, pin_batch_partials]

@@ -16,7 +16,7 @@ from tests import oracle_pins as pins
 _orig = {n: getattr(A, n) for n in ("split_bounds", "kv_rows", "attention_rows",
                                      "split_partials_rows", "merge_partials", "head_pairs",
                                      "split_bounds_ceil", "split_states_rows",
-                                     "merge_states")}
+                                     "merge_states", "attention_partials")}
 
 
 def _bounds_ceil_equal(seqlen, num_splits):
@@ -167,7 +167,16 @@ def _merge_states_sum_acc(m, l, acc):
     return out
 
 
+def _batch_partials_splits_reversed(q, k, v, cu, heads, kv_heads, ns, scale, layout="packed",
+                                    pairs=None):
+    # partials and LSEs stored in reverse split order: every merge stays exact,
+    # only the per-split layout the workspace is compared against is wrong
+    op, lse = _orig["attention_partials"](q, k, v, cu, heads, kv_heads, ns, scale, layout, pairs)
+    return op[:, :, ::-1, :], lse[:, ::-1, :]
+
+
 MUTANTS = {
+    "batch_partials_splits_reversed": ("attention_partials", _batch_partials_splits_reversed),
     "ceil_bounds_floor_size": ("split_bounds_ceil", _ceil_bounds_floor_size),
     "ceil_bounds_proportional": ("split_bounds_ceil", _ceil_bounds_proportional),
     "states_natural_exp": ("split_states_rows", _states_natural_exp),
@@ -193,7 +202,7 @@ MUTANTS = {
 _ORDER = [pins.pin_closed_forms, pins.pin_metamorphic, pins.pin_split_bounds,
           pins.pin_split_bounds_ceil, pins.pin_states_closed_forms, pins.pin_torch_sdpa,
           pins.pin_states_sdpa, pins.pin_decimal_bruteforce, pins.pin_states_decimal,
-          pins.pin_split_invariant]
+          pins.pin_split_invariant, pins.pin_batch_partials]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
