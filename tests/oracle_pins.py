@@ -472,6 +472,62 @@ def pin_batch_partials(orc):
                         assert abs(lse[b, s, h] - ref_lse) < 1e-12, (layout, b, h, s)
 
 
+def pin_batch_states(orc):
+    """attention_states (MiniInfer's format) on varlen batches whose offsets do
+    not start at 0, both layouts, split counts past some lengths: over split
+    s of flash_decode_splitk.py's ceil-equal bounds (size = ceil(L/ns) keys
+    from s*size, cut at L), acc_s / l_s is torch float64 SDPA over the
+    split's keys, m_s + log2(l_s) is scipy's logsumexp of the natural scaled
+    scores times log2(e), and m_s the largest base-2 scaled score; an empty
+    split holds (-inf, 0, 0)."""
+    from scipy.special import logsumexp
+    rng = _rng(12)
+    log2e = 1.0 / math.log(2.0)
+    for layout in ("packed", "bhsd"):
+        for (H, Hkv, D, lens, ns, off) in [(4, 2, 8, [9, 13, 3], 5, 3), (6, 3, 16, [20, 11], 4, 0),
+                                           (8, 1, 4, [6], 8, 2)]:
+            B, G = len(lens), H // Hkv
+            q = rng.standard_normal((B, H, D))
+            scale = 0.3
+            cu = [off]
+            for L in lens:
+                cu.append(cu[-1] + L)
+            if layout == "packed":
+                kv_k = rng.standard_normal((cu[-1] + 2, Hkv, D))
+                kv_v = rng.standard_normal((cu[-1] + 2, Hkv, D))
+                cu_arg = cu
+                rows = lambda kv, b, j: kv[cu[b]:cu[b + 1], j]
+            else:
+                S = max(lens) + 1
+                kv_k = rng.standard_normal((B, Hkv, S, D))
+                kv_v = rng.standard_normal((B, Hkv, S, D))
+                cu_arg = [0]
+                for L in lens:
+                    cu_arg.append(cu_arg[-1] + L)
+                rows = lambda kv, b, j: kv[b, j, :lens[b]]
+            m, l, acc = orc.attention_states(q, kv_k, kv_v, cu_arg, H, Hkv, ns, scale,
+                                             layout=layout)
+            assert m.shape == (B, H, ns) and l.shape == (B, H, ns) and acc.shape == (B, H, ns, D)
+            for b, L in enumerate(lens):
+                size = -(-L // ns)
+                for h in range(H):
+                    kr, vr = rows(kv_k, b, h // G), rows(kv_v, b, h // G)
+                    for s in range(ns):
+                        a, e = min(s * size, L), min(s * size + size, L)
+                        if e <= a:
+                            assert m[b, h, s] == -np.inf and l[b, h, s] == 0, (layout, b, h, s)
+                            assert not acc[b, h, s].any(), (layout, b, h, s)
+                            continue
+                        ref = _sdpa(q[b:b + 1, h:h + 1], kr[None, None, a:e], vr[None, None, a:e],
+                                    scale, 1)[0, 0]
+                        assert np.abs(acc[b, h, s] / l[b, h, s] - ref).max() < 1e-12, \
+                            (layout, b, h, s)
+                        x = scale * (kr[a:e] @ q[b, h])
+                        assert abs(m[b, h, s] + math.log2(l[b, h, s]) - logsumexp(x) * log2e) \
+                            < 1e-12, (layout, b, h, s)
+                        assert abs(m[b, h, s] - x.max() * log2e) < 1e-12, (layout, b, h, s)
+
+
 ALL_PINS = [pin_split_bounds, pin_closed_forms, pin_decimal_bruteforce, pin_torch_sdpa,
             pin_split_invariant, pin_metamorphic, pin_split_bounds_ceil, pin_states_decimal,
-            pin_states_closed_forms, pin_states_sdpa, pin_batch_partials]
+            pin_states_closed_forms, pin_states_sdpa, pin_batch_partials, pin_batch_states]

@@ -16,7 +16,8 @@ from tests import oracle_pins as pins
 _orig = {n: getattr(A, n) for n in ("split_bounds", "kv_rows", "attention_rows",
                                      "split_partials_rows", "merge_partials", "head_pairs",
                                      "split_bounds_ceil", "split_states_rows",
-                                     "merge_states", "attention_partials")}
+                                     "merge_states", "attention_partials",
+                                     "attention_states")}
 
 
 def _bounds_ceil_equal(seqlen, num_splits):
@@ -175,8 +176,16 @@ def _batch_partials_splits_reversed(q, k, v, cu, heads, kv_heads, ns, scale, lay
     return op[:, :, ::-1, :], lse[:, ::-1, :]
 
 
+def _batch_states_splits_reversed(q, k, v, cu, heads, kv_heads, ns, scale, layout="packed",
+                                  pairs=None):
+    # (m, l, acc) stored in reverse split order: every merge stays exact
+    m, l, acc = _orig["attention_states"](q, k, v, cu, heads, kv_heads, ns, scale, layout, pairs)
+    return m[:, :, ::-1], l[:, :, ::-1], acc[:, :, ::-1, :]
+
+
 MUTANTS = {
     "batch_partials_splits_reversed": ("attention_partials", _batch_partials_splits_reversed),
+    "batch_states_splits_reversed": ("attention_states", _batch_states_splits_reversed),
     "ceil_bounds_floor_size": ("split_bounds_ceil", _ceil_bounds_floor_size),
     "ceil_bounds_proportional": ("split_bounds_ceil", _ceil_bounds_proportional),
     "states_natural_exp": ("split_states_rows", _states_natural_exp),
@@ -202,7 +211,7 @@ MUTANTS = {
 _ORDER = [pins.pin_closed_forms, pins.pin_metamorphic, pins.pin_split_bounds,
           pins.pin_split_bounds_ceil, pins.pin_states_closed_forms, pins.pin_torch_sdpa,
           pins.pin_states_sdpa, pins.pin_decimal_bruteforce, pins.pin_states_decimal,
-          pins.pin_split_invariant, pins.pin_batch_partials]
+          pins.pin_split_invariant, pins.pin_batch_partials, pins.pin_batch_states]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
